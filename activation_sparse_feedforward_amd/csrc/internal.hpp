@@ -1,0 +1,64 @@
+// Kernel argument blocks and launch functions shared between the kernel
+// translation units and the C-ABI layer (host code only sees these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twell {
+
+struct PackArgs {
+  const void* x;         // [T x d]
+  const void* w_gate_t;  // [F x d]
+  int64_t T;
+  int32_t d, F, tile_n, C;
+  int32_t* count;  // [T][n_t]
+  uint8_t* idx;    // [T][n_t][C]
+  void* val;       // [T][n_t][C]
+  unsigned long long* stats;  // [2] or null
+  void* gate_dbg;             // [T x F] or null
+};
+
+struct FusedArgs {
+  const void* x;  // [T x d]
+  const int32_t* count;
+  const uint8_t* idx;
+  const void* val;
+  const void* w_up_t;  // [F x d]
+  const void* w_down;  // [F x d]
+  void* y;             // [T x d]
+  int64_t T;
+  int32_t d, F, tile_n, C;
+};
+
+// h[m, j] = ReLU(x[row(m)] . w_gate_t[j]) * (x[row(m)] . w_up_t[j]) for m < n_rows,
+// where row(m) = rows ? rows[m] : m and n_rows = n_rows_dev ? *n_rows_dev : M.
+struct GateUpArgs {
+  const void* x;
+  const void* w_gate_t;
+  const void* w_up_t;
+  void* h;  // [M x F] (compact rows)
+  const int32_t* rows;        // gather table or null
+  const int32_t* n_rows_dev;  // device row count or null
+  int64_t M;                  // host row count / upper bound
+  int32_t d, F;
+};
+
+// y[row(m), :] = h[m, :] . w_down  for m < n_rows (row(m) as above, scatter).
+struct DownArgs {
+  const void* h;       // [M x F]
+  const void* w_down;  // [F x d]
+  void* y;             // [T x d]
+  const int32_t* rows;
+  const int32_t* n_rows_dev;
+  int64_t M;
+  int32_t d, F;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
+hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s);
+hipError_t launch_fused_updown(const FusedArgs& a, int dtype, hipStream_t s);
+hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s);
+hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
+
+}  // namespace twell

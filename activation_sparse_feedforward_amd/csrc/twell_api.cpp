@@ -1,0 +1,172 @@
+// C ABI of libtwell: host-side validation and kernel dispatch.  Every check
+// happens before any HIP call, so a bad descriptor or pointer costs nothing on
+// the device and can be tested without a GPU.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "../../include/twell.h"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int64_t kIndexLimit = int64_t(1) << 31;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int elem_bytes(const twell_desc* d) { return d->dtype == TWELL_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+twell_status check_desc(const twell_desc* d) {
+  if (!d) return TWELL_EINVAL;
+  if (d->T < 0 || d->d_model <= 0 || d->d_ff <= 0 || d->tile_n <= 0 || d->slots <= 0) return TWELL_EINVAL;
+  if (d->dtype != TWELL_FP32 && d->dtype != TWELL_BF16) return TWELL_EINVAL;
+  if (d->d_ff % d->tile_n != 0) return TWELL_EINVAL;
+  if (d->slots > d->tile_n) return TWELL_EINVAL;
+  if (d->tile_n != 64 && d->tile_n != 128) return TWELL_EUNSUPPORTED;
+  if (d->dtype == TWELL_BF16) {
+    if (d->d_model % 512 != 0 || d->d_model > 4096) return TWELL_EUNSUPPORTED;
+  } else {
+    if (d->d_model % 256 != 0 || d->d_model > 2048) return TWELL_EUNSUPPORTED;
+  }
+  const int64_t widest = d->d_ff > d->d_model ? d->d_ff : d->d_model;
+  if (d->T > 0 && d->T > (kIndexLimit - 1) / widest) return TWELL_EUNSUPPORTED;
+  return TWELL_OK;
+}
+
+twell_status check_act(const twell_act& a) {
+  if (!a.count || !a.idx || !a.val) return TWELL_EINVAL;
+  if (!aligned4(a.count) || !aligned4(a.val)) return TWELL_EINVAL;
+  return TWELL_OK;
+}
+
+twell_status check_dense_ptr(const void* p) {
+  if (!p || !aligned16(p)) return TWELL_EINVAL;
+  return TWELL_OK;
+}
+
+#define TWELL_TRY(expr)                      \
+  do {                                       \
+    twell_status st_ = (expr);               \
+    if (st_ != TWELL_OK) return st_;         \
+  } while (0)
+
+twell_status from_hip(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+twell_status twell_sizes(const twell_desc* d, twell_sizes_t* out) {
+  TWELL_TRY(check_desc(d));
+  if (!out) return TWELL_EINVAL;
+  const size_t T = static_cast<size_t>(d->T);
+  const size_t n_t = static_cast<size_t>(d->d_ff / d->tile_n);
+  const size_t C = static_cast<size_t>(d->slots);
+  const size_t eb = static_cast<size_t>(elem_bytes(d));
+  out->count = T * n_t * 4;
+  out->idx = T * n_t * C;
+  out->val = T * n_t * C * eb;
+  out->ws_dense_fwd = T * static_cast<size_t>(d->d_ff) * eb;
+  return TWELL_OK;
+}
+
+twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                        int64_t* stats, void* gate_dbg, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_act(act));
+  if (stats && (reinterpret_cast<uintptr_t>(stats) & 7u)) return TWELL_EINVAL;
+  if (gate_dbg && !aligned4(gate_dbg)) return TWELL_EINVAL;
+  twell::PackArgs a{};
+  a.x = x;
+  a.w_gate_t = w_gate_t;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.F = d->d_ff;
+  a.tile_n = d->tile_n;
+  a.C = d->slots;
+  a.count = act.count;
+  a.idx = act.idx;
+  a.val = act.val;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.gate_dbg = gate_dbg;
+  return from_hip(twell::launch_gate_pack(a, d->dtype, static_cast<hipStream_t>(stream)));
+}
+
+twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, const void* w_up_t,
+                           const void* w_down, void* y, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_act(act));
+  TWELL_TRY(check_dense_ptr(w_up_t));
+  TWELL_TRY(check_dense_ptr(w_down));
+  TWELL_TRY(check_dense_ptr(y));
+  twell::FusedArgs a{};
+  a.x = x;
+  a.count = act.count;
+  a.idx = act.idx;
+  a.val = act.val;
+  a.w_up_t = w_up_t;
+  a.w_down = w_down;
+  a.y = y;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.F = d->d_ff;
+  a.tile_n = d->tile_n;
+  a.C = d->slots;
+  return from_hip(twell::launch_fused_updown(a, d->dtype, static_cast<hipStream_t>(stream)));
+}
+
+twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,
+                                 const void* w_up_t, const void* w_down, void* y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_dense_ptr(w_up_t));
+  TWELL_TRY(check_dense_ptr(w_down));
+  TWELL_TRY(check_dense_ptr(y));
+  TWELL_TRY(check_dense_ptr(ws));
+  twell_sizes_t sz;
+  TWELL_TRY(twell_sizes(d, &sz));
+  if (ws_bytes < sz.ws_dense_fwd) return TWELL_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  twell::GateUpArgs g{};
+  g.x = x;
+  g.w_gate_t = w_gate_t;
+  g.w_up_t = w_up_t;
+  g.h = ws;
+  g.rows = nullptr;
+  g.n_rows_dev = nullptr;
+  g.M = d->T;
+  g.d = d->d_model;
+  g.F = d->d_ff;
+  TWELL_TRY(from_hip(twell::launch_gateup(g, d->dtype, s)));
+  twell::DownArgs dn{};
+  dn.h = ws;
+  dn.w_down = w_down;
+  dn.y = y;
+  dn.rows = nullptr;
+  dn.n_rows_dev = nullptr;
+  dn.M = d->T;
+  dn.d = d->d_model;
+  dn.F = d->d_ff;
+  return from_hip(twell::launch_down(dn, d->dtype, s));
+}
+
+const char* twell_status_str(twell_status s) {
+  switch (s) {
+    case TWELL_OK: return "ok";
+    case TWELL_EINVAL: return "invalid argument (descriptor, pointer, alignment or workspace size)";
+    case TWELL_EUNSUPPORTED: return "shape or dtype not supported by this build";
+    case TWELL_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""TwELL FFN forward throughput on one MI355X.
+
+One step = one pass of the inference hot path over one batch: twell_pack
+(gate GEMM + ReLU + TwELL epilogue, one dispatch) then twell_ffn_fwd (fused
+up + down, one dispatch), on synthetic Llama-2B-shaped FFN inputs already
+resident in HBM (T=16384 tokens, d_model=2048, d_ff=8192, bf16, T_n=128,
+C=16, ~0.5% gate density).  Prints one JSON line.
+
+Also timed in the same run, the same way: the library's dense MFMA FFN
+(speed-up), per-kernel averages from HIP events on the launch stream (the
+roofline object), and the CPU oracle on a bounded token sample
+(cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload id (default: the 2B-class inference shape)")
+    ap.add_argument("--rho", type=float, default=None, help="override the gate density (sweep workload)")
+    ap.add_argument("--T", type=int, default=None, help="override the token count")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    return ap.parse_args()
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "activation_sparse_feedforward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str, per_launch_units: float):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summaries, only if they were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the CPU oracle's dense float64 forward on a bounded token sample."""
+    import numpy as np
+    from oracle import twell_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    x = inp["x"]
+    chunk = 256
+    done, t0 = 0, time.perf_counter()
+    while done < x.shape[0]:
+        O.ffn_forward(x[done:done + chunk], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])
+        done += chunk
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} tokens of the timed workload, oracle dense float64 forward "
+                      f"(NumPy matmul), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from activation_sparse_feedforward_amd import twell as T
+    from activation_sparse_feedforward_amd import workloads as W
+
+    T.library()  # fail loudly if the HIP library is missing
+    w = W.workload(args.config, T=args.T, rho=args.rho)
+    inp = W.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(raw):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(raw)).cuda()
+
+    x, wg, wu, wd = (dev(inp[k + "_raw"]) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
+    desc = T.Desc(w.T, w.d_model, w.d_ff, w.tile_n, w.slots, w.dtype)
+    act = T.alloc_act(desc)
+    y = torch.empty((w.T, w.d_model), dtype=dt, device="cuda")
+    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        T.twell_pack(desc, x, wg, act, stream=stream)
+        T.twell_ffn_fwd(desc, x, act, wu, wd, y, stream=stream)
+
+    # one checked pass (stats) before timing
+    T.twell_pack(desc, x, wg, act, stats=stats, stream=stream)
+    T.twell_ffn_fwd(desc, x, act, wu, wd, y, stream=stream)
+    torch.cuda.synchronize()
+    nnz, ovf = int(stats[1]), int(stats[0])
+    density = nnz / (w.T * w.d_ff)
+    if not torch.isfinite(y.float()).all():
+        raise RuntimeError("non-finite output")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        T.twell_pack(desc, x, wg, act, stream=stream)
+        ev[k][1].record(stream)
+        T.twell_ffn_fwd(desc, x, act, wu, wd, y, stream=stream)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pack_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    fused_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = wall / K * 1e3
+    value = w.T * K / wall
+
+    # dense comparator, timed the same way
+    dense = None
+    if not args.no_dense:
+        ws = torch.empty(T.sizes(desc)["ws_dense_fwd"], dtype=torch.uint8, device="cuda")
+        yd = torch.empty_like(y)
+        for _ in range(args.warmup):
+            T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, yd, ws, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, yd, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / K
+        flops = 6.0 * w.T * w.d_model * w.d_ff
+        dense = {"ms_per_step": round(dense_ms, 4), "tokens_per_s": round(w.T / dense_ms * 1e3, 1),
+                 "tflops": round(flops / dense_ms / 1e9, 1)}
+        del ws, yd
+
+    # roofline of the dominant kernel
+    peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    gate_flop = 2.0 * w.T * w.d_model * w.d_ff
+    eb = 2 if w.dtype == "bf16" else 4
+    # strictly required HBM bytes of the fused kernel: x, TwELL, every weight row touched once, y
+    twell_bytes = w.T * desc.n_t * (4 + w.slots * (1 + eb))
+    touched = 1.0 - (1.0 - density) ** w.T
+    fused_bytes = 2 * w.T * w.d_model * eb + twell_bytes + 2 * touched * w.d_ff * w.d_model * eb
+    gathered_bytes = nnz * 2 * w.d_model * eb
+    src = {"gate_pack": kernel_source_hash(["k_gate_pack.hip", "gemm_core.hpp", "common.hpp"]),
+           "fused_updown": kernel_source_hash(["k_fused_updown.hip", "common.hpp"])}
+    if pack_ms >= fused_ms:
+        ach = gate_flop / (pack_ms * 1e-3) / 1e12
+        roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(ach, 1), "peak": peak_mm,
+                "unit": "TFLOP/s", "frac": round(ach / peak_mm, 4),
+                "traffic": measured_traffic("gate_pack", src["gate_pack"], 1)}
+    else:
+        ach = fused_bytes / (fused_ms * 1e-3) / 1e9
+        roof = {"kernel": "fused_updown", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic("fused_updown", src["fused_updown"], 1)}
+
+    out = {
+        "metric": "TwELL FFN tokens/sec at 99.5% act. sparsity; speedup vs dense; % roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded PCG64; gate density set by a column-0 offset)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_ff": w.d_ff, "tile_n": w.tile_n,
+                   "slots": w.slots, "target_density": w.rho if w.density == "uniform" else w.density},
+        "roofline": roof,
+        "measured_density": round(density, 6),
+        "overflow_tiles": ovf,
+        "phases_ms": {"gate_pack": round(pack_ms, 4), "fused_updown": round(fused_ms, 4)},
+        "gate_pack_tflops": round(gate_flop / (pack_ms * 1e-3) / 1e12, 1),
+        "fused_updown": {"required_hbm_gbs": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                         "gathered_gbs": round(gathered_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                         "gathered_bytes": int(gathered_bytes), "required_bytes": int(fused_bytes)},
+        "dense_ffn": dense,
+        "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 3) if dense else None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * twell.h -- C ABI of libtwell: the TwELL activation-sparse gated FFN on MI355X (gfx950).
+ *
+ * The layer is  y = (ReLU(x W_gate) * (x W_up)) W_down  with a ReLU gate, whose
+ * output is mostly exact zeros.  Sources: the page "Sakana AI and NVIDIA
+ * introduce TwELL with CUDA kernels for 20.5% inference and 21.9% training"
+ * (noticias.mechatronicstore.cl), called P2 below, sections
+ *   "¿Qué hace distinto a TwELL frente a ELL clásico?"  (P2 §TwELL-vs-ELL):
+ *       tile-local packing built in the gate matmul's epilogue, the fused
+ *       up/down inference kernel, the hybrid ELL / dense-fallback format;
+ *   "Receta de entrenamiento: dos cambios y nada más"  (P2 §Receta):
+ *       ReLU gate, L1 penalty on the hidden activations;
+ *   "¿Cuál es el problema que TwELL resuelve?"  (P2 §Problema):
+ *       the dense Tensor-Core FFN that the sparse path is measured against.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layouts (all row-major, contiguous):
+ *      x, y, dy, dx     [T x d_model]          dtype
+ *      w_gate_t         [d_ff x d_model]        dtype   row j = neuron j's gate weights
+ *      w_up_t           [d_ff x d_model]        dtype   row j = neuron j's up weights
+ *      w_down           [d_ff x d_model]        dtype   row j = neuron j's output row
+ *    so g = x . w_gate_t^T, u = x . w_up_t^T, y = h . w_down.
+ *  - TwELL (twell_act), with n_t = d_ff / tile_n and C = slots:
+ *      count  int32  [T][n_t]        number of non-zeros of ReLU(g) in the (row, tile),
+ *                                    the TRUE number even when it exceeds C;
+ *      idx    uint8  [T][n_t][C]     tile-local column (0..tile_n-1) of each stored non-zero;
+ *      val    dtype  [T][n_t][C]     its value ReLU(g) rounded to dtype.
+ *    Slots s < min(count, C) hold the non-zeros in ascending column order; the
+ *    others hold idx 0 and value +0.  A value is a non-zero iff its rounded
+ *    (stored) value is not zero.
+ *  - Pointers: every array argument is a DEVICE pointer, 16-byte aligned,
+ *    owned by the caller.  The library never allocates or frees memory and
+ *    keeps no state between calls; scratch memory is passed in as `ws`.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default
+ *    stream).  All calls are asynchronous: they return after host-side
+ *    validation and the kernel launches, with no host synchronisation.
+ *  - Errors: TWELL_EINVAL for a bad descriptor, NULL / misaligned pointer or
+ *    too-small workspace (nothing is launched); TWELL_EUNSUPPORTED for a valid
+ *    shape this build has no kernel for; TWELL_EHIP when a launch fails.
+ *    Data-dependent conditions (overflowing tiles, dense-row cap exceeded) are
+ *    reported in device counters, never as host errors.
+ *  - Supported shapes: dtype BF16 with d_model % 512 == 0 and d_model <= 4096,
+ *    or FP32 with d_model % 256 == 0 and d_model <= 2048; tile_n in {64, 128};
+ *    d_ff % tile_n == 0; 1 <= slots <= tile_n; T >= 0 (T == 0 is a no-op);
+ *    T * d_ff < 2^31.
+ *  - Threading: calls are thread-safe (no global mutable state).
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TWELL_OK = 0,
+  TWELL_EINVAL = 1,
+  TWELL_EUNSUPPORTED = 2,
+  TWELL_EHIP = 3
+} twell_status;
+
+typedef enum { TWELL_FP32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+/* Problem descriptor.  T = tokens, d_model / d_ff = FFN widths, tile_n = TwELL
+ * tile width T_n (the gate matmul's N tile), slots = C. */
+typedef struct {
+  int64_t T;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t tile_n;
+  int32_t slots;
+  int32_t dtype; /* twell_dtype */
+} twell_desc;
+
+/* The three TwELL planes (device pointers, layouts above). */
+typedef struct {
+  int32_t* count;
+  uint8_t* idx;
+  void* val;
+} twell_act;
+
+/* Byte sizes of the TwELL planes and of the workspaces, for a descriptor. */
+typedef struct {
+  size_t count;        /* T * n_t * 4                                   */
+  size_t idx;          /* T * n_t * C                                   */
+  size_t val;          /* T * n_t * C * sizeof(dtype)                   */
+  size_t ws_dense_fwd; /* workspace of twell_dense_ffn_fwd: h [T x d_ff] */
+} twell_sizes_t;
+
+/* Fill *out for descriptor *d.  Host only; no device work.
+ * Returns TWELL_EINVAL / TWELL_EUNSUPPORTED like the compute calls would. */
+twell_status twell_sizes(const twell_desc* d, twell_sizes_t* out);
+
+/* Gate GEMM + ReLU + TwELL pack, in ONE kernel dispatch.
+ * [P2 §TwELL-vs-ELL: the sparse format is produced inside the epilogue of the
+ * gate matmul, with no extra launch and no dense write of the activations.]
+ *   x [T x d_model], w_gate_t [d_ff x d_model] (dtype)  ->  act (all three planes written).
+ * g accumulates in fp32; ReLU(g) is rounded to dtype before the non-zero test.
+ * stats  (device int64[2], nullable): ACCUMULATED (atomic add) with
+ *        [0] += number of (row, tile) pairs whose count exceeds slots,
+ *        [1] += sum of all counts (= non-zeros of ReLU(g));  zero it first.
+ * gate_dbg (device, nullable): if given, the same kernel also writes the dense
+ *        ReLU(g) [T x d_ff] in dtype (parity / debugging only; it is the dense
+ *        write-back the method exists to avoid, so leave it NULL when timing). */
+twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                        int64_t* stats, void* gate_dbg, void* stream);
+
+/* Fused up + down projection on TwELL input, in ONE kernel dispatch.
+ * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down
+ * projections together; the intermediate never reaches global memory.]
+ * For every row t and stored slot (neuron j = b*tile_n + idx, value a):
+ *   u = x[t] . w_up_t[j];  h = a * u;  y[t] += h * w_down[j]   (fp32 accumulate)
+ * y [T x d_model] is overwritten (stored in dtype).  A tile with count > slots
+ * contributes only its stored slots (the plain format is lossy there; the
+ * hybrid entry point is the remedy). */
+twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, const void* w_up_t,
+                           const void* w_down, void* y, void* stream);
+
+/* The library's own dense MFMA FFN, the baseline the sparse path is compared with.
+ * [P2 §Problema: GPUs are built for dense matrix products; the sparse path must
+ * beat the dense one.]
+ * Kernel 1: g = x w_gate, u = x w_up in one GEMM, epilogue h = ReLU(g) * u
+ *           stored to ws as dtype [T x d_ff];
+ * Kernel 2: y = h w_down (y overwritten, dtype).
+ * ws must hold twell_sizes().ws_dense_fwd bytes. */
+twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,
+                                 const void* w_up_t, const void* w_down, void* y, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* twell_status_str(twell_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */
