@@ -4,5 +4,5 @@ The compute path is libtwell.so (HIP kernels + C ABI, include/twell.h); the
 Python module ``twell`` is its thin ctypes binding.  ``workloads`` draws the
 seeded synthetic inputs.
 """
-from .twell import (Act, Desc, TwellError, alloc_act, library, sizes, status_str,  # noqa: F401
-                    twell_dense_ffn_fwd, twell_ffn_fwd, twell_pack)
+from .twell import (Act, Desc, Route, TwellError, alloc_act, alloc_route, library, sizes,  # noqa: F401
+                    status_str, twell_dense_ffn_fwd, twell_ffn_fwd, twell_ffn_fwd_hybrid, twell_pack)

@@ -27,8 +27,24 @@ struct FusedArgs {
   const void* w_up_t;  // [F x d]
   const void* w_down;  // [F x d]
   void* y;             // [T x d]
-  int64_t T;
+  const int32_t* rows;        // row list (ELL rows of the hybrid format) or null = all rows
+  const int32_t* n_rows_dev;  // device count of `rows` or null
+  int64_t T;                  // rows of x / y; also the upper bound of the row list
   int32_t d, F, tile_n, C;
+};
+
+// Hybrid router: flags[t] (1 = dense), ascending ell_rows / dense_rows lists,
+// n_rows = {n_ell, n_dense, n_dense_over_cap}.
+struct RouteArgs {
+  const int32_t* count;  // [T][n_t]
+  int64_t T;
+  int32_t n_t, C;
+  int64_t cap;           // at most this many dense rows are kept
+  uint8_t* flags;        // [T] scratch; final value 1 = kept dense, 0 = ELL
+  int32_t* block_dense;  // [ceil(T/256)] scratch
+  int32_t* ell_rows;     // [T]
+  int32_t* dense_rows;   // [cap]
+  int32_t* n_rows;       // [3]
 };
 
 // h[m, j] = ReLU(x[row(m)] . w_gate_t[j]) * (x[row(m)] . w_up_t[j]) for m < n_rows,
@@ -60,5 +76,6 @@ hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fused_updown(const FusedArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 }  // namespace twell

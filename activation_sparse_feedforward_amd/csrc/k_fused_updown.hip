@@ -94,8 +94,10 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
   __shared__ int2 list_all[kWavesPerBlock][kListCap];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  if (t >= p.T) return;  // whole wave exits together; no block barrier below
+  const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
+  if (i_row >= n_rows) return;  // whole wave exits together; no block barrier below
+  const int64_t t = p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row;
   int2* list = list_all[wave];
   const int d = p.d, C = p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;

@@ -1,0 +1,109 @@
+// Hybrid row router.
+//
+// The TwELL page ("Sakana AI and NVIDIA introduce TwELL with CUDA kernels...",
+// section "¿Qué hace distinto a TwELL frente a ELL clásico?") routes each row
+// at run time either to a compact ELL store or, when the row has too many
+// non-zeros, to a dense fallback.  Reading used here: a row is dense iff one
+// of its tiles holds more non-zeros than the C slots (count > C), i.e. iff the
+// ELL store would drop entries of that row.
+//
+// Two small kernels, no host synchronisation, deterministic output:
+//   route_flags:   one thread per row -> flag[t] (1 = dense) and the number
+//                  of dense rows of each 256-row block;
+//   route_scatter: one thread per row -> the row's rank among dense rows
+//                  (sum of earlier blocks + in-block scan), then ascending
+//                  ell_rows / dense_rows lists and the counters.
+// At most `cap` dense rows are kept (the fallback's workspace bound); dense
+// rows past the cap go to the ELL list (lossy there) and are counted in
+// n_rows[2] so the caller can see it.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace twell {
+
+constexpr int kRouteBlock = 256;
+
+__global__ __launch_bounds__(kRouteBlock) void route_flags_kernel(RouteArgs p) {
+  __shared__ int wsum[kRouteBlock / kWave];
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  int dense = 0;
+  if (t < p.T) {
+    const int32_t* c = p.count + t * p.n_t;
+    int mx = 0;
+    for (int b = 0; b < p.n_t; ++b) mx = max(mx, c[b]);
+    dense = mx > p.C ? 1 : 0;
+    p.flags[t] = static_cast<uint8_t>(dense);
+  }
+  int s = dense;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < kRouteBlock / kWave; ++w) tot += wsum[w];
+    p.block_dense[blockIdx.x] = tot;
+  }
+}
+
+__global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(RouteArgs p) {
+  __shared__ int red[kRouteBlock / kWave];
+  __shared__ int wpre[kRouteBlock / kWave];
+  const int nblk = static_cast<int>((p.T + kRouteBlock - 1) / kRouteBlock);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // dense rows in earlier blocks (block 0 also totals every block)
+  const int upto = blockIdx.x == 0 ? nblk : static_cast<int>(blockIdx.x);
+  int part = 0;
+  for (int i = threadIdx.x; i < upto; i += kRouteBlock) part += p.block_dense[i];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  int sum_upto = 0;
+  for (int w = 0; w < kRouteBlock / kWave; ++w) sum_upto += red[w];
+  const int before_block = blockIdx.x == 0 ? 0 : sum_upto;
+
+  // in-block exclusive scan of the flags (ascending t)
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  const int f = t < p.T ? static_cast<int>(p.flags[t]) : 0;
+  int incl = f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wpre[wave] = incl;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += wpre[w];
+  const int64_t dense_before = before_block + wave_off + incl - f;
+  if (t < p.T) {
+    const int64_t kept_before = dense_before < p.cap ? dense_before : p.cap;
+    if (f && dense_before < p.cap) {
+      p.dense_rows[dense_before] = static_cast<int32_t>(t);
+      p.flags[t] = 1;
+    } else {
+      p.ell_rows[t - kept_before] = static_cast<int32_t>(t);
+      p.flags[t] = 0;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int64_t total = sum_upto;
+    const int64_t kept = total < p.cap ? total : p.cap;
+    p.n_rows[0] = static_cast<int32_t>(p.T - kept);
+    p.n_rows[1] = static_cast<int32_t>(kept);
+    p.n_rows[2] = static_cast<int32_t>(total - kept);
+  }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  const unsigned nblk = static_cast<unsigned>((a.T + kRouteBlock - 1) / kRouteBlock);
+  hipLaunchKernelGGL(route_flags_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace twell

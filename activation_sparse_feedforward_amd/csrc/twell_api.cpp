@@ -45,6 +45,22 @@ twell_status check_dense_ptr(const void* p) {
   return TWELL_OK;
 }
 
+size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+// Workspace layout of the hybrid forward: router block counts, then the dense
+// rows' hidden activations h [max_dense_rows x d_ff].
+struct HybridWs {
+  size_t block_dense, h, total;
+};
+HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
+  HybridWs w{};
+  const size_t nblk = static_cast<size_t>((d->T + 255) / 256);
+  w.block_dense = 0;
+  w.h = align256(nblk * 4);
+  w.total = w.h + align256(static_cast<size_t>(max_dense_rows) * d->d_ff * elem_bytes(d));
+  return w;
+}
+
 #define TWELL_TRY(expr)                      \
   do {                                       \
     twell_status st_ = (expr);               \
@@ -57,9 +73,9 @@ twell_status from_hip(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_
 
 extern "C" {
 
-twell_status twell_sizes(const twell_desc* d, twell_sizes_t* out) {
+twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_sizes_t* out) {
   TWELL_TRY(check_desc(d));
-  if (!out) return TWELL_EINVAL;
+  if (!out || max_dense_rows < 0) return TWELL_EINVAL;
   const size_t T = static_cast<size_t>(d->T);
   const size_t n_t = static_cast<size_t>(d->d_ff / d->tile_n);
   const size_t C = static_cast<size_t>(d->slots);
@@ -68,6 +84,8 @@ twell_status twell_sizes(const twell_desc* d, twell_sizes_t* out) {
   out->idx = T * n_t * C;
   out->val = T * n_t * C * eb;
   out->ws_dense_fwd = T * static_cast<size_t>(d->d_ff) * eb;
+  const HybridWs hw = hybrid_ws(d, max_dense_rows);
+  out->ws_hybrid = hw.total;
   return TWELL_OK;
 }
 
@@ -106,6 +124,8 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
   TWELL_TRY(check_dense_ptr(w_down));
   TWELL_TRY(check_dense_ptr(y));
   twell::FusedArgs a{};
+  a.rows = nullptr;
+  a.n_rows_dev = nullptr;
   a.x = x;
   a.count = act.count;
   a.idx = act.idx;
@@ -121,6 +141,82 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
   return from_hip(twell::launch_fused_updown(a, d->dtype, static_cast<hipStream_t>(stream)));
 }
 
+twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                                  const void* w_up_t, const void* w_down, void* y, const twell_route* route,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (!route || route->max_dense_rows < 0) return TWELL_EINVAL;
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_act(act));
+  TWELL_TRY(check_dense_ptr(w_up_t));
+  TWELL_TRY(check_dense_ptr(w_down));
+  TWELL_TRY(check_dense_ptr(y));
+  if (!route->ell_rows || !route->n_rows || !route->row_kind) return TWELL_EINVAL;
+  if (route->max_dense_rows > 0 && !route->dense_rows) return TWELL_EINVAL;
+  if (!aligned4(route->ell_rows) || !aligned4(route->n_rows) ||
+      (route->dense_rows && !aligned4(route->dense_rows)))
+    return TWELL_EINVAL;
+  const HybridWs hw = hybrid_ws(d, route->max_dense_rows);
+  if (!ws || !aligned16(ws) || ws_bytes < hw.total) return TWELL_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+
+  twell::RouteArgs r{};
+  r.count = act.count;
+  r.T = d->T;
+  r.n_t = d->d_ff / d->tile_n;
+  r.C = d->slots;
+  r.cap = route->max_dense_rows;
+  r.flags = route->row_kind;
+  r.block_dense = reinterpret_cast<int32_t*>(wsb + hw.block_dense);
+  r.ell_rows = route->ell_rows;
+  r.dense_rows = route->dense_rows;
+  r.n_rows = route->n_rows;
+  TWELL_TRY(from_hip(twell::launch_route(r, s)));
+
+  twell::FusedArgs f{};
+  f.x = x;
+  f.count = act.count;
+  f.idx = act.idx;
+  f.val = act.val;
+  f.w_up_t = w_up_t;
+  f.w_down = w_down;
+  f.y = y;
+  f.rows = route->ell_rows;
+  f.n_rows_dev = route->n_rows + 0;
+  f.T = d->T;
+  f.d = d->d_model;
+  f.F = d->d_ff;
+  f.tile_n = d->tile_n;
+  f.C = d->slots;
+  TWELL_TRY(from_hip(twell::launch_fused_updown(f, d->dtype, s)));
+
+  if (route->max_dense_rows == 0) return TWELL_OK;
+  twell::GateUpArgs g{};
+  g.x = x;
+  g.w_gate_t = w_gate_t;
+  g.w_up_t = w_up_t;
+  g.h = wsb + hw.h;
+  g.rows = route->dense_rows;
+  g.n_rows_dev = route->n_rows + 1;
+  g.M = route->max_dense_rows;
+  g.d = d->d_model;
+  g.F = d->d_ff;
+  TWELL_TRY(from_hip(twell::launch_gateup(g, d->dtype, s)));
+  twell::DownArgs dn{};
+  dn.h = wsb + hw.h;
+  dn.w_down = w_down;
+  dn.y = y;
+  dn.rows = route->dense_rows;
+  dn.n_rows_dev = route->n_rows + 1;
+  dn.M = route->max_dense_rows;
+  dn.d = d->d_model;
+  dn.F = d->d_ff;
+  return from_hip(twell::launch_down(dn, d->dtype, s));
+}
+
 twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,
                                  const void* w_up_t, const void* w_down, void* y, void* ws,
                                  size_t ws_bytes, void* stream) {
@@ -133,7 +229,7 @@ twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void*
   TWELL_TRY(check_dense_ptr(y));
   TWELL_TRY(check_dense_ptr(ws));
   twell_sizes_t sz;
-  TWELL_TRY(twell_sizes(d, &sz));
+  TWELL_TRY(twell_sizes(d, 0, &sz));
   if (ws_bytes < sz.ws_dense_fwd) return TWELL_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   twell::GateUpArgs g{};

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libtwell.so")
 TWELL_OK, TWELL_EINVAL, TWELL_EUNSUPPORTED, TWELL_EHIP = 0, 1, 2, 3
 TWELL_FP32, TWELL_BF16 = 0, 1
 
-EXPORTED = ("twell_sizes", "twell_pack", "twell_ffn_fwd", "twell_dense_ffn_fwd", "twell_status_str")
+EXPORTED = ("twell_sizes", "twell_pack", "twell_ffn_fwd", "twell_ffn_fwd_hybrid", "twell_dense_ffn_fwd",
+            "twell_status_str")
 
 
 class TwellError(RuntimeError):
@@ -40,9 +41,14 @@ class CAct(ctypes.Structure):
     _fields_ = [("count", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("val", ctypes.c_void_p)]
 
 
+class CRoute(ctypes.Structure):
+    _fields_ = [("ell_rows", ctypes.c_void_p), ("dense_rows", ctypes.c_void_p), ("n_rows", ctypes.c_void_p),
+                ("row_kind", ctypes.c_void_p), ("max_dense_rows", ctypes.c_int64)]
+
+
 class CSizes(ctypes.Structure):
     _fields_ = [("count", ctypes.c_size_t), ("idx", ctypes.c_size_t), ("val", ctypes.c_size_t),
-                ("ws_dense_fwd", ctypes.c_size_t)]
+                ("ws_dense_fwd", ctypes.c_size_t), ("ws_hybrid", ctypes.c_size_t)]
 
 
 _lib = None
@@ -58,8 +64,10 @@ def library() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         P, I64, SZ, ST = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         D = ctypes.POINTER(CDesc)
+        R = ctypes.POINTER(CRoute)
         sig = {
-            "twell_sizes": (ST, [D, ctypes.POINTER(CSizes)]),
+            "twell_sizes": (ST, [D, I64, ctypes.POINTER(CSizes)]),
+            "twell_ffn_fwd_hybrid": (ST, [D, P, P, CAct, P, P, P, R, P, SZ, P]),
             "twell_pack": (ST, [D, P, P, CAct, P, P, P]),
             "twell_ffn_fwd": (ST, [D, P, CAct, P, P, P, P]),
             "twell_dense_ffn_fwd": (ST, [D, P, P, P, P, P, P, SZ, P]),
@@ -68,7 +76,6 @@ def library() -> ctypes.CDLL:
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
             f.restype, f.argtypes = res, args
-        del I64
         _lib = lib
     return _lib
 
@@ -110,9 +117,21 @@ class Act(NamedTuple):
     val: torch.Tensor    # dtype [T, n_t, C]
 
 
-def sizes(desc: Desc) -> dict:
+class Route(NamedTuple):
+    """Row routing of the hybrid format as device tensors."""
+    ell_rows: torch.Tensor    # int32 [T]
+    dense_rows: torch.Tensor  # int32 [max_dense_rows]
+    n_rows: torch.Tensor      # int32 [3]: n_ell, n_dense, dense rows over the cap
+    row_kind: torch.Tensor    # uint8 [T]: 1 = dense fallback
+
+    @property
+    def max_dense_rows(self) -> int:
+        return int(self.dense_rows.numel())
+
+
+def sizes(desc: Desc, max_dense_rows: int = 0) -> dict:
     out = CSizes()
-    st = library().twell_sizes(ctypes.byref(desc.c()), ctypes.byref(out))
+    st = library().twell_sizes(ctypes.byref(desc.c()), ctypes.c_int64(max_dense_rows), ctypes.byref(out))
     if st != TWELL_OK:
         raise TwellError("twell_sizes", st)
     return {k: int(getattr(out, k)) for k, _ in CSizes._fields_}
@@ -122,6 +141,13 @@ def alloc_act(desc: Desc, device="cuda") -> Act:
     return Act(torch.empty((desc.T, desc.n_t), dtype=torch.int32, device=device),
                torch.empty((desc.T, desc.n_t, desc.slots), dtype=torch.uint8, device=device),
                torch.empty((desc.T, desc.n_t, desc.slots), dtype=desc.torch_dtype, device=device))
+
+
+def alloc_route(desc: Desc, max_dense_rows: int, device="cuda") -> Route:
+    return Route(torch.empty(max(desc.T, 1), dtype=torch.int32, device=device),
+                 torch.empty(max_dense_rows, dtype=torch.int32, device=device),
+                 torch.zeros(3, dtype=torch.int32, device=device),
+                 torch.empty(max(desc.T, 1), dtype=torch.uint8, device=device))
 
 
 # ----------------------------------------------------------------------------- checks
@@ -154,6 +180,14 @@ def _act(desc: Desc, act: Act) -> CAct:
                 _ptr(act.val, "val", sz["val"], desc.torch_dtype))
 
 
+def _route(desc: Desc, route: Route) -> CRoute:
+    cap = route.max_dense_rows
+    return CRoute(_ptr(route.ell_rows, "ell_rows", desc.T * 4, torch.int32),
+                  _ptr(route.dense_rows, "dense_rows", cap * 4, torch.int32) if cap else 0,
+                  _ptr(route.n_rows, "n_rows", 12, torch.int32),
+                  _ptr(route.row_kind, "row_kind", desc.T, torch.uint8), cap)
+
+
 def _check(fn: str, st: int):
     if st != TWELL_OK:
         raise TwellError(fn, st)
@@ -180,6 +214,21 @@ def twell_ffn_fwd(desc: Desc, x, act: Act, w_up_t, w_down, y, stream=None):
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
         _ptr(y, "y", desc.T * desc.d_model * e, dt), _stream(stream)))
+
+
+def twell_ffn_fwd_hybrid(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_down, y, route: Route, ws, stream=None):
+    """Router + fused TwELL path on ELL rows + dense MFMA fallback on dense rows."""
+    e = 2 if desc.dtype == "bf16" else 4
+    dt = desc.torch_dtype
+    need = sizes(desc, route.max_dense_rows)["ws_hybrid"]
+    cr = _route(desc, route)
+    _check("twell_ffn_fwd_hybrid", library().twell_ffn_fwd_hybrid(
+        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
+        _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
+        _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
+        _ptr(y, "y", desc.T * desc.d_model * e, dt), ctypes.byref(cr), _ptr(ws, "ws", need),
+        ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
 
 
 def twell_dense_ffn_fwd(desc: Desc, x, w_gate_t, w_up_t, w_down, y, ws, stream=None):

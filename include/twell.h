@@ -83,17 +83,28 @@ typedef struct {
   void* val;
 } twell_act;
 
+/* Row routing of the hybrid format (device arrays owned by the caller).
+ * Written by twell_ffn_fwd_hybrid; read by the backward. */
+typedef struct {
+  int32_t* ell_rows;      /* [T]               rows served from TwELL, ascending           */
+  int32_t* dense_rows;    /* [max_dense_rows]  rows served by the dense fallback, ascending */
+  int32_t* n_rows;        /* [3]  {n_ell, n_dense, dense rows beyond max_dense_rows}        */
+  uint8_t* row_kind;      /* [T]  1 = row went to the dense fallback, 0 = TwELL             */
+  int64_t max_dense_rows; /* capacity of dense_rows and of the fallback workspace           */
+} twell_route;
+
 /* Byte sizes of the TwELL planes and of the workspaces, for a descriptor. */
 typedef struct {
-  size_t count;        /* T * n_t * 4                                   */
-  size_t idx;          /* T * n_t * C                                   */
-  size_t val;          /* T * n_t * C * sizeof(dtype)                   */
-  size_t ws_dense_fwd; /* workspace of twell_dense_ffn_fwd: h [T x d_ff] */
+  size_t count;        /* T * n_t * 4                                        */
+  size_t idx;          /* T * n_t * C                                        */
+  size_t val;          /* T * n_t * C * sizeof(dtype)                        */
+  size_t ws_dense_fwd; /* workspace of twell_dense_ffn_fwd: h [T x d_ff]      */
+  size_t ws_hybrid;    /* workspace of twell_ffn_fwd_hybrid (max_dense_rows)  */
 } twell_sizes_t;
 
-/* Fill *out for descriptor *d.  Host only; no device work.
+/* Fill *out for descriptor *d and a dense-row capacity (>= 0).  Host only.
  * Returns TWELL_EINVAL / TWELL_EUNSUPPORTED like the compute calls would. */
-twell_status twell_sizes(const twell_desc* d, twell_sizes_t* out);
+twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_sizes_t* out);
 
 /* Gate GEMM + ReLU + TwELL pack, in ONE kernel dispatch.
  * [P2 §TwELL-vs-ELL: the sparse format is produced inside the epilogue of the
@@ -119,6 +130,24 @@ twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t
  * hybrid entry point is the remedy). */
 twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, const void* w_up_t,
                            const void* w_down, void* y, void* stream);
+
+/* Hybrid forward: row router + fused TwELL path on ELL rows + dense MFMA
+ * fallback on dense rows.  [P2 §TwELL-vs-ELL: for training, whose sparsity is
+ * far from uniform, each row goes at run time either to a compact ELL store
+ * or to a dense fallback when it has too many non-zeros.]
+ * act must come from twell_pack on the same x and w_gate_t.
+ * Kernels (same stream, no host synchronisation):
+ *   1-2. router: a row is dense iff some tile has count > slots; ascending
+ *        ell_rows / dense_rows, n_rows, row_kind.  At most max_dense_rows
+ *        rows are kept dense; further dense rows are served (lossily) from
+ *        TwELL and counted in n_rows[2].
+ *   3.   fused up/down (as twell_ffn_fwd) over ell_rows;
+ *   4-5. dense gate|up GEMM over the gathered dense rows (h = ReLU(g) * u,
+ *        recomputed, kept in ws), then the down GEMM scattered into y.
+ * y [T x d_model] is overwritten.  ws: twell_sizes(d, max_dense_rows).ws_hybrid bytes. */
+twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                                  const void* w_up_t, const void* w_down, void* y, const twell_route* route,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* The library's own dense MFMA FFN, the baseline the sparse path is compared with.
  * [P2 §Problema: GPUs are built for dense matrix products; the sparse path must

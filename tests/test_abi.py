@@ -25,7 +25,7 @@ def _st(**kw):
     base = dict(T=256, d_model=512, d_ff=1024, tile_n=128, slots=16, dtype=T.TWELL_BF16)
     base.update(kw)
     d = T.CDesc(base["T"], base["d_model"], base["d_ff"], base["tile_n"], base["slots"], base["dtype"])
-    return T.library().twell_sizes(ctypes.byref(d), ctypes.byref(T.CSizes()))
+    return T.library().twell_sizes(ctypes.byref(d), ctypes.c_int64(0), ctypes.byref(T.CSizes()))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -54,6 +54,10 @@ def test_sizes_values():
     assert s["idx"] == 16384 * 64 * 16
     assert s["val"] == 16384 * 64 * 16 * 2
     assert s["ws_dense_fwd"] == 16384 * 8192 * 2
+    h = T.sizes(T.Desc(16384, 2048, 8192, 128, 16, "bf16"), max_dense_rows=1000)
+    assert h["ws_hybrid"] >= 1000 * 8192 * 2 + 64 * 4
+    d = T.Desc(16, 512, 1024, 128, 16, "bf16").c()
+    assert T.library().twell_sizes(ctypes.byref(d), ctypes.c_int64(-1), ctypes.byref(T.CSizes())) == T.TWELL_EINVAL
 
 
 def test_null_and_misaligned_pointers_rejected_before_launch():
@@ -69,6 +73,11 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.twell_dense_ffn_fwd(ctypes.byref(d), P, P, P, P, P, P, 100, None) == T.TWELL_EINVAL  # ws too small
     assert lib.twell_dense_ffn_fwd(ctypes.byref(d), P, P, P, P, P, None, 1 << 30, None) == T.TWELL_EINVAL
     assert lib.twell_pack(None, P, P, act, None, None, None) == T.TWELL_EINVAL
+    r = T.CRoute(P, P, P, P, 10)
+    assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, None, P, 1 << 30, None) == T.TWELL_EINVAL
+    assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, ctypes.byref(r), P, 16, None) == T.TWELL_EINVAL
+    r0 = T.CRoute(P, 0, P, P, 10)  # capacity without a dense_rows array
+    assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, ctypes.byref(r0), P, 1 << 30, None) == T.TWELL_EINVAL
 
 
 def test_empty_batch_is_a_noop():

@@ -1,0 +1,112 @@
+"""GPU parity of the hybrid forward (router + fused TwELL rows + dense MFMA
+fallback rows) against the CPU oracle, through the C ABI.
+
+  * route lists, counters and row kinds are exact against the oracle router
+    applied to the kernel's own counts (with the dense-row cap applied);
+  * y: ELL rows within tol of the oracle's TwELL forward on the kernel's
+    TwELL; dense rows within tol of the oracle's dense FFN; and every row
+    within tol of the dense FFN when no row exceeds the cap.
+"""
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_feedforward_amd import twell as T
+from activation_sparse_feedforward_amd import workloads as W
+from oracle import twell_oracle as O
+from _helpers import desc_for, dev, host64, poison_, say
+
+pytestmark = pytest.mark.gpu
+TOL = {"fp32": 1e-5, "bf16": 1e-2}
+
+
+def run_hybrid(w, cap, rows=None, label=""):
+    say(f"[gpu case] hybrid {label} {w.name} T={w.T} cap={cap}")
+    inp = W.make_inputs(w)
+    desc = desc_for(w)
+    x, wg, wu, wd = (dev(inp[k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
+    act = T.alloc_act(desc)
+    T.twell_pack(desc, x, wg, act)
+    route = T.alloc_route(desc, cap)
+    for t in route:
+        poison_(t)
+    ws = torch.empty(T.sizes(desc, cap)["ws_hybrid"], dtype=torch.uint8, device="cuda")
+    y = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
+    T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, ws)
+    torch.cuda.synchronize()
+
+    count = act.count.cpu().numpy()
+    idx = act.idx.cpu().numpy()
+    val = host64(act.val)
+    n_rows = route.n_rows.cpu().numpy()
+    dense, ell_all, dense_all = O.route(count, w.slots)
+    kept = dense_all[:cap]
+    over = dense_all[cap:]
+    ell_exp = np.sort(np.concatenate([ell_all, over])).astype(np.int32)
+    assert n_rows.tolist() == [len(ell_exp), len(kept), len(over)]
+    np.testing.assert_array_equal(route.ell_rows.cpu().numpy()[:len(ell_exp)], ell_exp)
+    if cap:
+        np.testing.assert_array_equal(route.dense_rows.cpu().numpy()[:len(kept)], kept)
+    kind = np.zeros(w.T, np.uint8)
+    kind[kept] = 1
+    np.testing.assert_array_equal(route.row_kind.cpu().numpy()[:w.T], kind)
+
+    yh = host64(y)
+    sel = np.arange(w.T) if rows is None else np.asarray(rows)
+    sel_ell = np.intersect1d(sel, ell_exp)
+    sel_dense = np.intersect1d(sel, kept)
+    tol = TOL[w.dtype]
+    f = O.ffn_forward(inp["x"][sel], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])
+    scale = max(np.abs(f["y"]).max(), 1e-30)
+    if sel_ell.size:
+        y_ref = O.twell_forward(inp["x"][sel_ell], count[sel_ell], idx[sel_ell], val[sel_ell], w.tile_n,
+                                inp["w_up_t"], inp["w_down"])
+        assert np.abs(yh[sel_ell] - y_ref).max() <= tol * scale
+    if sel_dense.size:
+        y_ref = O.ffn_forward(inp["x"][sel_dense], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])["y"]
+        assert np.abs(yh[sel_dense] - y_ref).max() <= tol * scale
+    if len(over) == 0:
+        # the hybrid format is exact: every row matches the dense FFN
+        assert np.abs(yh[sel] - f["y"]).max() <= tol * scale
+    say(f"   ok: n_ell={n_rows[0]} n_dense={n_rows[1]} over_cap={n_rows[2]}")
+    return dict(y=y, route=route, act=act, inp=inp, desc=desc)
+
+
+@pytest.mark.parametrize("T_,cap", [(1500, 512), (257, 300), (64, 64)])
+def test_hybrid_lognormal_tail(T_, cap):
+    run_hybrid(W.workload(4, T=T_), cap, label="lognormal")
+
+
+def test_hybrid_cap_exceeded_routes_rest_to_ell():
+    w = W.workload(5, T=600, rho=0.05)   # ~1.5% of rows overflow C=16 at 5% density
+    r = run_hybrid(w, 3, label="cap=3")
+    assert int(r["route"].n_rows[2]) > 0
+
+
+def test_hybrid_cap_zero_equals_plain_fused():
+    w = W.workload(4, T=700)
+    r = run_hybrid(w, 0, label="cap=0")
+    y2 = torch.empty_like(r["y"])
+    x, wu, wd = (dev(r["inp"][k + "_raw"], w.dtype) for k in ("x", "w_up_t", "w_down"))
+    T.twell_ffn_fwd(r["desc"], x, r["act"], wu, wd, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
+
+
+def test_hybrid_all_rows_dense():
+    w = W.workload(5, T=300, rho=0.3)   # every row overflows
+    r = run_hybrid(w, 300, label="all dense")
+    assert int(r["route"].n_rows[0]) == 0
+
+
+def test_hybrid_fp32():
+    import dataclasses
+    w = dataclasses.replace(W.workload(1), slots=2)  # few slots: some rows go dense
+    run_hybrid(w, 256, label="fp32 C=2")
+
+
+def test_hybrid_full_size_sampled():
+    w = W.workload(4)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(w.T - 256, w.T), rng.choice(w.T, 256, replace=False)]))
+    run_hybrid(w, 1024, rows=rows, label="full c4")
