@@ -70,7 +70,9 @@ struct KRowLoader {
 // Operand with MN contiguous: the matrix is stored [K x MN] row-major (ld = MN
 // elements) and the tile is R columns (mn0 ..) by one 128-byte K slice.  Each
 // thread loads four K rows of one 16-byte MN chunk and writes them transposed
-// into the K-contiguous LDS layout.  K rows past `k_total` read as 0.
+// into the K-contiguous LDS layout.  K rows may go through an indirection
+// table (gathered rows); K rows past `k_total` and columns past `mn_total`
+// read as 0 (mn_total must be a multiple of 16 bytes' worth of elements).
 // ---------------------------------------------------------------------------
 template <class E, int R>
 struct MNColLoader {
@@ -83,13 +85,18 @@ struct MNColLoader {
   int64_t ld;
   int64_t k_total;
   int64_t mn0;
+  int64_t mn_total;
+  const int32_t* rows;
   u32x4_t regs[kPer][4];
 
-  __device__ __forceinline__ void init(const void* ptr, int64_t ld_, int64_t mn0_, int64_t k_total_) {
+  __device__ __forceinline__ void init(const void* ptr, int64_t ld_, int64_t mn0_, int64_t mn_total_,
+                                       int64_t k_total_, const int32_t* rows_ = nullptr) {
     base = static_cast<const char*>(ptr);
     ld = ld_;
     mn0 = mn0_;
+    mn_total = mn_total_;
     k_total = k_total_;
+    rows = rows_;
   }
   __device__ __forceinline__ void load(int kt) {
     const int tid = threadIdx.x;
@@ -97,11 +104,13 @@ struct MNColLoader {
     for (int p = 0; p < kPer; ++p) {
       const int u = tid + p * kThreads;
       const int mnc = u % kMnChunks, kq = u / kMnChunks;
+      const bool col_ok = mn0 + mnc * E::kPer16B < mn_total;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int64_t k = static_cast<int64_t>(kt) * kSliceElems + kq * 4 + i;
-        if (k < k_total) {
-          const char* a = base + (k * ld + mn0 + mnc * E::kPer16B) * E::kBytes;
+        if (col_ok && k < k_total) {
+          const int64_t kr = rows ? static_cast<int64_t>(rows[k]) : k;
+          const char* a = base + (kr * ld + mn0 + mnc * E::kPer16B) * E::kBytes;
           regs[p][i] = *reinterpret_cast<const u32x4_t*>(a);
         } else {
           regs[p][i] = u32x4_t{0, 0, 0, 0};
@@ -109,48 +118,40 @@ struct MNColLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(char* lds, int row_base) const;
-};
-
-template <>
-__device__ __forceinline__ void MNColLoader<EBf16, 128>::store(char* lds, int row_base) const {
-  const int tid = threadIdx.x;
+  __device__ __forceinline__ void store(char* lds, int row_base) const {
+    const int tid = threadIdx.x;
 #pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int u = tid + p * kThreads;
-    const int mnc = u % kMnChunks, kq = u / kMnChunks;
+    for (int p = 0; p < kPer; ++p) {
+      const int u = tid + p * kThreads;
+      const int mnc = u % kMnChunks, kq = u / kMnChunks;
+      if constexpr (E::kBytes == 2) {
+        // four K rows x eight bf16 columns -> eight 8-byte K runs, one per column
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      uint32_t lo, hi;
-      if ((e & 1) == 0) {
-        lo = (regs[p][0][w] & 0xffffu) | (regs[p][1][w] << 16);
-        hi = (regs[p][2][w] & 0xffffu) | (regs[p][3][w] << 16);
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          uint32_t lo, hi;
+          if ((e & 1) == 0) {
+            lo = (regs[p][0][w] & 0xffffu) | (regs[p][1][w] << 16);
+            hi = (regs[p][2][w] & 0xffffu) | (regs[p][3][w] << 16);
+          } else {
+            lo = (regs[p][0][w] >> 16) | (regs[p][1][w] & 0xffff0000u);
+            hi = (regs[p][2][w] >> 16) | (regs[p][3][w] & 0xffff0000u);
+          }
+          const int row = row_base + mnc * 8 + e;
+          *reinterpret_cast<u32x2_t*>(lds + lds_off(row, kq >> 1) + ((kq & 1) << 3)) = u32x2_t{lo, hi};
+        }
       } else {
-        lo = (regs[p][0][w] >> 16) | (regs[p][1][w] & 0xffff0000u);
-        hi = (regs[p][2][w] >> 16) | (regs[p][3][w] & 0xffff0000u);
+        // four K rows x four fp32 columns -> four 16-byte K runs, one per column
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = row_base + mnc * 4 + e;
+          *reinterpret_cast<u32x4_t*>(lds + lds_off(row, kq)) =
+              u32x4_t{regs[p][0][e], regs[p][1][e], regs[p][2][e], regs[p][3][e]};
+        }
       }
-      const int row = row_base + mnc * 8 + e;
-      *reinterpret_cast<u32x2_t*>(lds + lds_off(row, kq >> 1) + ((kq & 1) << 3)) = u32x2_t{lo, hi};
     }
   }
-}
-
-template <>
-__device__ __forceinline__ void MNColLoader<EF32, 128>::store(char* lds, int row_base) const {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const int u = tid + p * kThreads;
-    const int mnc = u % kMnChunks, kq = u / kMnChunks;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = row_base + mnc * 4 + e;
-      *reinterpret_cast<u32x4_t*>(lds + lds_off(row, kq)) =
-          u32x4_t{regs[p][0][e], regs[p][1][e], regs[p][2][e], regs[p][3][e]};
-    }
-  }
-}
+};
 
 // ---------------------------------------------------------------------------
 // Fragment reads (see mfma_k16 for the lane -> k assignment).
@@ -176,19 +177,22 @@ struct Acc {
 // MFMAs of slice kt.
 // ---------------------------------------------------------------------------
 template <class E, int BN, class LA, class LB>
-__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* lds, Acc<BN>& acc) {
+__device__ __forceinline__ void gemm_mainloop(LA& la, LB& lb, int nk, char* lds, Acc<BN>& acc,
+                                              bool accumulate = false) {
   constexpr int kWN = BN / 32;
   constexpr int kSteps = 128 / E::kBytes / 16;
   char* ldsA = lds;
   char* ldsB = lds + kBM * 128;
   const int lane = threadIdx.x & 63;
   const int wrow = (threadIdx.x >> 6) * 64;
+  if (!accumulate) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kWN; ++nb)
+      for (int nb = 0; nb < kWN; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc.c[mb][nb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc.c[mb][nb][r] = 0.f;
+  }
   if (nk <= 0) return;
   la.load(0);
   lb.load(0);

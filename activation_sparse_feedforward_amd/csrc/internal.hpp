@@ -71,11 +71,45 @@ struct DownArgs {
   int32_t d, F;
 };
 
+// Backward of the hybrid-format FFN (sparse rows: k_bwd.hip, dense rows: k_bwd_dense.hip).
+struct BwdArgs {
+  const void* x;
+  const void* dy;
+  const int32_t* count;
+  const uint8_t* idx;
+  const void* val;
+  const void* w_gate_t;
+  const void* w_up_t;
+  const void* w_down;
+  const int32_t* ell_rows;    // route of the forward
+  const int32_t* dense_rows;
+  const int32_t* n_rows;      // device {n_ell, n_dense, over_cap}
+  int64_t T, cap;
+  int32_t d, F, tile_n, C;
+  float l1;
+  void* dx;
+  float* dw_gate_t;
+  float* dw_up_t;
+  float* dw_down;
+  // workspace
+  int32_t* blk_hist;    // [ceil(T/64)][F]
+  int32_t* neuron_off;  // [F + 1]
+  int32_t* pos;         // [T][n_t][C]
+  float4* recs;         // [T * n_t * C] {t, dg, du, h}
+  float* g_d;           // [cap][F]
+  float* u_d;           // [cap][F]
+  void* dg_d;           // [cap][F] dtype
+  void* du_d;
+  void* h_d;
+};
+
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
 hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fused_updown(const FusedArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_bwd_sparse(const BwdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_bwd_dense(const BwdArgs& a, int dtype, hipStream_t s);
 
 }  // namespace twell

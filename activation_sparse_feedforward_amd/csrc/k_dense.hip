@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads, 2) void down_kernel(DownArgs p) {
   KRowLoader<E, kBM> la;
   la.init(p.h, p.F, m0, n_rows, nullptr);
   MNColLoader<E, 128> lb;
-  lb.init(p.w_down, p.d, n0, p.F);
+  lb.init(p.w_down, p.d, n0, p.d, p.F);
   Acc<128> acc;
   gemm_mainloop<E, 128>(la, lb, p.F / KRowLoader<E, kBM>::kSliceElems, lds, acc);
 

@@ -61,6 +61,29 @@ HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
   return w;
 }
 
+// Workspace layout of the backward.
+struct BwdWs {
+  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, total;
+};
+BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
+  BwdWs w{};
+  const size_t T = static_cast<size_t>(d->T), F = static_cast<size_t>(d->d_ff);
+  const size_t slots = T * static_cast<size_t>(d->d_ff / d->tile_n) * static_cast<size_t>(d->slots);
+  const size_t cap = static_cast<size_t>(max_dense_rows), eb = static_cast<size_t>(elem_bytes(d));
+  size_t o = 0;
+  w.blk_hist = o;   o += align256(((T + 63) / 64) * F * 4);
+  w.neuron_off = o; o += align256((F + 1) * 4);
+  w.pos = o;        o += align256(slots * 4);
+  w.recs = o;       o += align256(slots * 16);
+  w.g_d = o;        o += align256(cap * F * 4);
+  w.u_d = o;        o += align256(cap * F * 4);
+  w.dg_d = o;       o += align256(cap * F * eb);
+  w.du_d = o;       o += align256(cap * F * eb);
+  w.h_d = o;        o += align256(cap * F * eb);
+  w.total = o;
+  return w;
+}
+
 #define TWELL_TRY(expr)                      \
   do {                                       \
     twell_status st_ = (expr);               \
@@ -86,6 +109,7 @@ twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_size
   out->ws_dense_fwd = T * static_cast<size_t>(d->d_ff) * eb;
   const HybridWs hw = hybrid_ws(d, max_dense_rows);
   out->ws_hybrid = hw.total;
+  out->ws_bwd = bwd_ws(d, max_dense_rows).total;
   return TWELL_OK;
 }
 
@@ -215,6 +239,66 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
   dn.d = d->d_model;
   dn.F = d->d_ff;
   return from_hip(twell::launch_down(dn, d->dtype, s));
+}
+
+twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, const twell_route* route,
+                           const void* w_gate_t, const void* w_up_t, const void* w_down, const void* dy,
+                           float l1_coef, void* dx, float* dw_gate_t, float* dw_up_t, float* dw_down,
+                           void* ws, size_t ws_bytes, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (!route || route->max_dense_rows < 0) return TWELL_EINVAL;
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_dense_ptr(w_up_t));
+  TWELL_TRY(check_dense_ptr(w_down));
+  TWELL_TRY(check_dense_ptr(dw_gate_t));
+  TWELL_TRY(check_dense_ptr(dw_up_t));
+  TWELL_TRY(check_dense_ptr(dw_down));
+  const BwdWs bw = bwd_ws(d, route->max_dense_rows);
+  if (!ws || !aligned16(ws) || ws_bytes < bw.total) return TWELL_EINVAL;
+  if (d->T > 0) {
+    TWELL_TRY(check_dense_ptr(x));
+    TWELL_TRY(check_dense_ptr(dy));
+    TWELL_TRY(check_dense_ptr(dx));
+    TWELL_TRY(check_act(act));
+    if (!route->ell_rows || !route->n_rows) return TWELL_EINVAL;
+    if (route->max_dense_rows > 0 && !route->dense_rows) return TWELL_EINVAL;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+  twell::BwdArgs a{};
+  a.x = x;
+  a.dy = dy;
+  a.count = act.count;
+  a.idx = act.idx;
+  a.val = act.val;
+  a.w_gate_t = w_gate_t;
+  a.w_up_t = w_up_t;
+  a.w_down = w_down;
+  a.ell_rows = route->ell_rows;
+  a.dense_rows = route->dense_rows;
+  a.n_rows = route->n_rows;
+  a.T = d->T;
+  a.cap = d->T > 0 ? route->max_dense_rows : 0;
+  a.d = d->d_model;
+  a.F = d->d_ff;
+  a.tile_n = d->tile_n;
+  a.C = d->slots;
+  a.l1 = l1_coef;
+  a.dx = dx;
+  a.dw_gate_t = dw_gate_t;
+  a.dw_up_t = dw_up_t;
+  a.dw_down = dw_down;
+  a.blk_hist = reinterpret_cast<int32_t*>(wsb + bw.blk_hist);
+  a.neuron_off = reinterpret_cast<int32_t*>(wsb + bw.neuron_off);
+  a.pos = reinterpret_cast<int32_t*>(wsb + bw.pos);
+  a.recs = reinterpret_cast<float4*>(wsb + bw.recs);
+  a.g_d = reinterpret_cast<float*>(wsb + bw.g_d);
+  a.u_d = reinterpret_cast<float*>(wsb + bw.u_d);
+  a.dg_d = wsb + bw.dg_d;
+  a.du_d = wsb + bw.du_d;
+  a.h_d = wsb + bw.h_d;
+  TWELL_TRY(from_hip(twell::launch_bwd_sparse(a, d->dtype, s)));
+  return from_hip(twell::launch_bwd_dense(a, d->dtype, s));
 }
 
 twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,

@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libtwell.so")
 TWELL_OK, TWELL_EINVAL, TWELL_EUNSUPPORTED, TWELL_EHIP = 0, 1, 2, 3
 TWELL_FP32, TWELL_BF16 = 0, 1
 
-EXPORTED = ("twell_sizes", "twell_pack", "twell_ffn_fwd", "twell_ffn_fwd_hybrid", "twell_dense_ffn_fwd",
-            "twell_status_str")
+EXPORTED = ("twell_sizes", "twell_pack", "twell_ffn_fwd", "twell_ffn_fwd_hybrid", "twell_ffn_bwd",
+            "twell_dense_ffn_fwd", "twell_status_str")
 
 
 class TwellError(RuntimeError):
@@ -48,7 +48,7 @@ class CRoute(ctypes.Structure):
 
 class CSizes(ctypes.Structure):
     _fields_ = [("count", ctypes.c_size_t), ("idx", ctypes.c_size_t), ("val", ctypes.c_size_t),
-                ("ws_dense_fwd", ctypes.c_size_t), ("ws_hybrid", ctypes.c_size_t)]
+                ("ws_dense_fwd", ctypes.c_size_t), ("ws_hybrid", ctypes.c_size_t), ("ws_bwd", ctypes.c_size_t)]
 
 
 _lib = None
@@ -68,6 +68,7 @@ def library() -> ctypes.CDLL:
         sig = {
             "twell_sizes": (ST, [D, I64, ctypes.POINTER(CSizes)]),
             "twell_ffn_fwd_hybrid": (ST, [D, P, P, CAct, P, P, P, R, P, SZ, P]),
+            "twell_ffn_bwd": (ST, [D, P, CAct, R, P, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]),
             "twell_pack": (ST, [D, P, P, CAct, P, P, P]),
             "twell_ffn_fwd": (ST, [D, P, CAct, P, P, P, P]),
             "twell_dense_ffn_fwd": (ST, [D, P, P, P, P, P, P, SZ, P]),
@@ -228,6 +229,24 @@ def twell_ffn_fwd_hybrid(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_down, y, r
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
         _ptr(y, "y", desc.T * desc.d_model * e, dt), ctypes.byref(cr), _ptr(ws, "ws", need),
+        ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
+
+
+def twell_ffn_bwd(desc: Desc, x, act: Act, route: Route, w_gate_t, w_up_t, w_down, dy, l1_coef: float,
+                  dx, dw_gate_t, dw_up_t, dw_down, ws, stream=None):
+    """Backward of the hybrid-format FFN with the L1 activation penalty (see include/twell.h)."""
+    e = 2 if desc.dtype == "bf16" else 4
+    dt = desc.torch_dtype
+    need = sizes(desc, route.max_dense_rows)["ws_bwd"]
+    cr = _route(desc, route)
+    wbytes = desc.d_ff * desc.d_model
+    _check("twell_ffn_bwd", library().twell_ffn_bwd(
+        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt), _act(desc, act), ctypes.byref(cr),
+        _ptr(w_gate_t, "w_gate_t", wbytes * e, dt), _ptr(w_up_t, "w_up_t", wbytes * e, dt),
+        _ptr(w_down, "w_down", wbytes * e, dt), _ptr(dy, "dy", desc.T * desc.d_model * e, dt),
+        ctypes.c_float(l1_coef), _ptr(dx, "dx", desc.T * desc.d_model * e, dt),
+        _ptr(dw_gate_t, "dw_gate_t", wbytes * 4, torch.float32), _ptr(dw_up_t, "dw_up_t", wbytes * 4, torch.float32),
+        _ptr(dw_down, "dw_down", wbytes * 4, torch.float32), _ptr(ws, "ws", need),
         ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
 
 

@@ -100,6 +100,7 @@ typedef struct {
   size_t val;          /* T * n_t * C * sizeof(dtype)                        */
   size_t ws_dense_fwd; /* workspace of twell_dense_ffn_fwd: h [T x d_ff]      */
   size_t ws_hybrid;    /* workspace of twell_ffn_fwd_hybrid (max_dense_rows)  */
+  size_t ws_bwd;       /* workspace of twell_ffn_bwd (max_dense_rows)         */
 } twell_sizes_t;
 
 /* Fill *out for descriptor *d and a dense-row capacity (>= 0).  Host only.
@@ -148,6 +149,25 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
 twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
                                   const void* w_up_t, const void* w_down, void* y, const twell_route* route,
                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the hybrid-format FFN, reusing the forward's TwELL and route.
+ * [P2 §Receta: ReLU gate and an L1 term on the hidden activations;
+ *  P2 §TwELL-vs-ELL: the training format is the hybrid one.]
+ * Loss whose gradients are returned:  L = sum(y * dy) + l1_coef * sum|h|,
+ * with h = ReLU(g) * u the hidden activation feeding w_down (sign(0) = 0,
+ * ReLU'(0) = 0).  Given dy [T x d_model] (dtype):
+ *   dx        [T x d_model]  dtype, overwritten (every row);
+ *   dw_gate_t, dw_up_t, dw_down  [d_ff x d_model] fp32, overwritten.
+ * act and route must be those of the twell_pack / twell_ffn_fwd_hybrid call on
+ * the same x.  Rows in route->ell_rows use only their stored TwELL slots (a
+ * row the forward served lossily from TwELL is differentiated the same way);
+ * rows in route->dense_rows are recomputed densely on MFMA.
+ * Deterministic: the weight gradients of each neuron are summed in ascending
+ * token order.  ws: twell_sizes(d, route->max_dense_rows).ws_bwd bytes. */
+twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, const twell_route* route,
+                           const void* w_gate_t, const void* w_up_t, const void* w_down, const void* dy,
+                           float l1_coef, void* dx, float* dw_gate_t, float* dw_up_t, float* dw_down,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* The library's own dense MFMA FFN, the baseline the sparse path is compared with.
  * [P2 §Problema: GPUs are built for dense matrix products; the sparse path must
