@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
+    ap.add_argument("--train-config", type=int, default=4, help="workload of the training-step measurement")
+    ap.add_argument("--max-dense-rows", type=int, default=1024)
     return ap.parse_args()
 
 
@@ -85,6 +88,54 @@ def cpu_baseline(inp, budget_s: float):
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} tokens of the timed workload, oracle dense float64 forward "
                       f"(NumPy matmul), {dt:.1f} s"}
+
+
+def train_step(T, W, args, steps, warmup):
+    """Time one training step of the FFN layer on the training workload:
+    twell_pack + twell_ffn_fwd_hybrid + twell_ffn_bwd (HIP events per phase)."""
+    import numpy as np
+    import torch
+    w = W.workload(args.train_config)
+    inp = W.make_inputs(w, with_dy=True)
+
+    def dev(raw):
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, wg, wu, wd, dy = (dev(inp[k + "_raw"]) for k in ("x", "w_gate_t", "w_up_t", "w_down", "dy"))
+    desc = T.Desc(w.T, w.d_model, w.d_ff, w.tile_n, w.slots, w.dtype)
+    cap = args.max_dense_rows
+    act = T.alloc_act(desc)
+    route = T.alloc_route(desc, cap)
+    sz = T.sizes(desc, cap)
+    wsf = torch.empty(sz["ws_hybrid"], dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(sz["ws_bwd"], dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty_like(y)
+    dws = [torch.empty((w.d_ff, w.d_model), dtype=torch.float32, device="cuda") for _ in range(3)]
+    stream = torch.cuda.current_stream()
+
+    def run(ev=None):
+        if ev: ev[0].record(stream)
+        T.twell_pack(desc, x, wg, act, stream=stream)
+        if ev: ev[1].record(stream)
+        T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, wsf, stream=stream)
+        if ev: ev[2].record(stream)
+        T.twell_ffn_bwd(desc, x, act, route, wg, wu, wd, dy, w.l1_coef, dx, *dws, wsb, stream=stream)
+        if ev: ev[3].record(stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for k in range(steps):
+        run(evs[k])
+    torch.cuda.synchronize()
+    ph = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
+    n_rows = route.n_rows.cpu().tolist()
+    tot = sum(ph)
+    return {"workload": w.name, "ms_per_step": round(tot, 4), "tokens_per_s": round(w.T / tot * 1e3, 1),
+            "phases_ms": {"pack": round(ph[0], 4), "hybrid_fwd": round(ph[1], 4), "bwd": round(ph[2], 4)},
+            "n_ell": n_rows[0], "n_dense": n_rows[1], "dense_over_cap": n_rows[2]}
 
 
 def main():
@@ -220,6 +271,10 @@ def main():
         "dense_ffn": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 3) if dense else None,
     }
+    if not args.no_train:
+        del act, y
+        torch.cuda.empty_cache()
+        out["training"] = train_step(T, W, args, max(3, K // 2), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
