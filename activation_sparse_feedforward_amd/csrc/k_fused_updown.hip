@@ -73,6 +73,34 @@ template <> struct Vec<EF32> {
   }
 };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// This lane's part of the dot product of two rows held as NV 16-byte chunks
+// (x and w in storage form).  bf16: packed-pair dot products (v_dot2 with an
+// fp32 accumulator) in four independent chains, summed at the end; fp32:
+// plain FMAs in the same four-chain order.  (The bf16 pairs are taken from a
+// whole-vector cast: casting an element of the 32-bit vector directly was
+// compiled to always read element 0.)
+template <class E, int NV>
+__device__ __forceinline__ float lane_dot(const u32x4_t* w, const u32x4_t* x) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if constexpr (E::kBytes == 2) {
+      const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w[v]);
+      const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, x[v]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wh[2 * i], wh[2 * i + 1]},
+                                                 bf16x2_t{xh[2 * i], xh[2 * i + 1]}, acc[i], false);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[v][i]), __uint_as_float(x[v][i]), acc[i]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // Inclusive prefix sum over the wave (Hillis-Steele with shuffles); small and
 // only run once per 64 tiles.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -169,18 +197,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
       }
       float hq[kU];
 #pragma unroll
-      for (int q = 0; q < kU; ++q) {
-        float part = 0.f;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          float w[kN], xv[kN];
-          Vec<E>::unpack(wu[q][v], w);
-          Vec<E>::unpack(xs[v], xv);
-#pragma unroll
-          for (int i = 0; i < kN; ++i) part = fmaf(xv[i], w[i], part);
-        }
-        hq[q] = part;
-      }
+      for (int q = 0; q < kU; ++q) hq[q] = lane_dot<E, NV>(wu[q], xs);
 #pragma unroll
       for (int q = 0; q < kU; ++q) hq[q] = aa[q] * wave_sum(hq[q]);
 #pragma unroll
@@ -202,6 +219,174 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
   for (int v = 0; v < NV; ++v) yr[v * kWave + lane] = Vec<E>::pack(yf[v]);
 }
 
+// Lockstep variant (d_model up to 2048 in bf16): a workgroup of 16 waves, each
+// owning TPW tokens, walks the TwELL tiles in chunks with a workgroup barrier
+// between chunks.  Every resident workgroup therefore sweeps the neuron tiles
+// in roughly the same order at the same time, so the weight rows of the
+// current tiles (~1 MB per tile at the 2B shape) are shared through each
+// XCD's L2 instead of each wave fetching random rows from the MALL; more
+// tokens per workgroup keeps the workgroups in tighter step.  x[t] lives in
+// LDS (this frees the VGPRs for the fp32 y accumulators of TPW tokens).  Per
+// token the arithmetic is exactly that of fused_updown_kernel (same order), so
+// results are bitwise identical.
+constexpr int kSyncWaves = 16;
+constexpr int kSyncList = 128;  // list entries per wave per chunk
+
+template <class E, int NV, int TPW, int kU>
+__global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
+  constexpr int kN = Vec<E>::N;
+  constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
+  extern __shared__ __align__(16) char smem[];
+  u32x4_t* xl = reinterpret_cast<u32x4_t*>(smem);  // [16 waves][TPW][kRowVec]
+  int4* list_all = reinterpret_cast<int4*>(smem + kSyncWaves * TPW * kRowVec * 16);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
+  int4* list = list_all + wave * kSyncList;
+  u32x4_t* xw = xl + wave * TPW * kRowVec;
+  const int d = p.d, C = p.C, tile_n = p.tile_n;
+  const int n_t = p.F / tile_n;
+
+  int64_t tk[TPW];
+  bool act[TPW];
+  float yf[TPW][NV][kN];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int64_t i_row = (static_cast<int64_t>(blockIdx.x) * kSyncWaves + wave) * TPW + k;
+    act[k] = i_row < n_rows;  // idle tokens: the wave still takes part in the barriers
+    tk[k] = act[k] ? (p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row) : 0;
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + tk[k] * d * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      xw[k * kRowVec + v * kWave + lane] = act[k] ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kN; ++i) yf[k][v][i] = 0.f;
+    }
+  }
+  // lanes of the list builder: lane = tile_in_chunk * TPW + token
+  const int chunk_tiles = max(1, min(kWave / TPW, kSyncList / (C * TPW)));
+  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+    __syncthreads();
+    const int b = b0 + lane / TPW, kl = lane % TPW;
+    int cnt = 0;
+    int64_t tl = 0;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k)
+      if (kl == k) {
+        tl = tk[k];
+        if (act[k] && lane < chunk_tiles * TPW && b < n_t) cnt = max(0, min(p.count[tk[k] * n_t + b], C));
+      }
+    const int incl = wave_incl_scan(cnt, lane);
+    const int total = min(__shfl(incl, 63), kSyncList);
+    const int off = incl - cnt;
+    if (cnt > 0) {
+      const int64_t rec = (tl * n_t + b) * C;
+      // off + cnt <= chunk_tiles * TPW * C <= kSyncList by the launch's choice of TPW
+      for (int s = 0; s < cnt && off + s < kSyncList; ++s) {
+        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
+        list[off + s] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s)), kl, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e0 = 0; e0 < total; e0 += kU) {
+      const int nq = min(kU, total - e0);
+      int jj[kU], kk[kU];
+      float aa[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int4 ent = list[min(e0 + q, total - 1)];
+        jj[q] = __builtin_amdgcn_readfirstlane(ent.x);
+        aa[q] = (q < nq) ? __int_as_float(__builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
+        kk[q] = __builtin_amdgcn_readfirstlane(ent.z);
+      }
+      u32x4_t wu[kU][NV], wd[kU][NV];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int64_t ro = int64_t(jj[q]) * d * E::kBytes;
+        const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
+        const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
+        if (q < nq) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            wu[q][v] = ur[v * kWave + lane];
+            wd[q][v] = dr[v * kWave + lane];
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) wu[q][v] = wd[q][v] = u32x4_t{0, 0, 0, 0};
+        }
+      }
+      float hq[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const u32x4_t* xq = xw + kk[q] * kRowVec;
+        u32x4_t xv[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xv[v] = xq[v * kWave + lane];
+        hq[q] = lane_dot<E, NV>(wu[q], xv);
+      }
+#pragma unroll
+      for (int q = 0; q < kU; ++q) hq[q] = aa[q] * wave_sum(hq[q]);
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+          if (kk[q] == k) {  // wave-uniform
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+              float w[kN];
+              Vec<E>::unpack(wd[q][v], w);
+#pragma unroll
+              for (int i = 0; i < kN; ++i) yf[k][v][i] = fmaf(hq[q], w[i], yf[k][v][i]);
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    if (act[k]) {
+      u32x4_t* yr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.y) + tk[k] * d * E::kBytes);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) yr[v * kWave + lane] = Vec<E>::pack(yf[k][v]);
+    }
+  }
+}
+
+template <int NV, int TPW, int EB>
+constexpr size_t sync_lds_bytes() {
+  return static_cast<size_t>(kSyncWaves) * TPW * NV * kWave * 16 + kSyncWaves * kSyncList * 16;
+}
+
+template <class E, int NV, int TPW, int kU>
+static hipError_t launch_sync_cfg(const FusedArgs& a, hipStream_t s) {
+  constexpr size_t lds = sync_lds_bytes<NV, TPW, E::kBytes>();
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  const int64_t per_block = static_cast<int64_t>(kSyncWaves) * TPW;
+  dim3 grid(static_cast<unsigned>((a.T + per_block - 1) / per_block));
+  hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+  return hipGetLastError();
+}
+
+// Tokens per wave: as many fp32 y rows as fit beside the loads in 128 VGPRs,
+// and no more than the per-chunk list holds when one tile of each token is
+// full (TPW * C <= kSyncList, so every chunk of >= 1 tile fits).
+template <class E, int NV>
+static hipError_t launch_sync_t(const FusedArgs& a, hipStream_t s) {
+  constexpr int kMax = NV * Vec<E>::N <= 16 ? 4 : 2;
+  const int fit = kSyncList / a.C;
+  if (kMax >= 4 && fit >= 4) return launch_sync_cfg<E, NV, 4, 1>(a, s);
+  if (fit >= 2) return launch_sync_cfg<E, NV, 2, 1>(a, s);
+  return launch_sync_cfg<E, NV, 1, 1>(a, s);
+}
+
 template <class E, int NV>
 static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((a.T + kWavesPerBlock - 1) / kWavesPerBlock));
@@ -213,10 +398,10 @@ template <class E>
 static hipError_t launch_fused_e(const FusedArgs& a, hipStream_t s) {
   const int nv = a.d / (kWave * Vec<E>::N);
   switch (nv) {
-    case 1: return launch_fused_t<E, 1>(a, s);
-    case 2: return launch_fused_t<E, 2>(a, s);
-    case 3: return launch_fused_t<E, 3>(a, s);
-    case 4: return launch_fused_t<E, 4>(a, s);
+    case 1: return launch_sync_t<E, 1>(a, s);
+    case 2: return launch_sync_t<E, 2>(a, s);
+    case 3: return launch_sync_t<E, 3>(a, s);
+    case 4: return launch_sync_t<E, 4>(a, s);
     case 5: return launch_fused_t<E, 5>(a, s);
     case 6: return launch_fused_t<E, 6>(a, s);
     case 7: return launch_fused_t<E, 7>(a, s);

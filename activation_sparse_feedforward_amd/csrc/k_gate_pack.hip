@@ -4,112 +4,225 @@
 // kernels...", section "¿Qué hace distinto a TwELL frente a ELL clásico?"):
 // the sparse format is produced inside the epilogue of the gate matmul, the
 // activation columns are cut into tiles equal to the matmul's N tile, and the
-// non-zeros are packed locally per tile.  Here the N tile of a workgroup IS
-// one TwELL tile (BN = T_n) and every wave owns whole rows of it, so each
-// (row, tile) is compacted straight from the MFMA accumulators: a wavefront
-// ballot per 32-column block gives the non-zero mask of two rows at once, and
-// popcounts of the masks give every non-zero its slot in ascending column
-// order -- no atomics, no LDS round trip, no dense store of ReLU(g).
+// non-zeros are packed locally per tile.  Here every wave owns complete rows
+// of one TwELL tile in its MFMA accumulators, so each (row, tile) is compacted
+// straight from registers: a wavefront ballot per 32-column block gives the
+// non-zero mask of two rows at once, and popcounts of the masks give every
+// non-zero its slot in ascending column order -- no atomics and no dense
+// store of ReLU(g); the compact records are assembled in LDS and leave with
+// wide stores.
+//
+// T_n = 128 uses the 256 x 256 direct-to-LDS core (gemm256.hpp); T_n = 64 the
+// 256 x 64 register-staged core (gemm_core.hpp).
+#include <algorithm>
+
+#include "gemm256.hpp"
 #include "gemm_core.hpp"
 #include "internal.hpp"
 
 namespace twell {
 
-template <class E, int BN>
-__global__ __launch_bounds__(kThreads, 2) void gate_pack_kernel(PackArgs p) {
-  extern __shared__ __align__(16) char lds[];
-  const int b = blockIdx.x;                       // TwELL tile index == N tile
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int n_t = p.F / BN;
-
-  KRowLoader<E, kBM> la;
-  KRowLoader<E, BN> lb;
-  la.init(p.x, p.d, m0, p.T, nullptr);
-  lb.init(p.w_gate_t, p.d, static_cast<int64_t>(b) * BN, p.F, nullptr);
-  Acc<BN> acc;
-  gemm_mainloop<E, BN>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
-
-  constexpr int kWN = BN / 32;
+// Compact one wave's accumulators (rows wrow0 .. wrow0 + 32*MB, TwELL tile b of
+// width 32*KWN) into TwELL.  Register r of a 32x32 block holds, in lanes 0-31,
+// 32 columns of one row and, in lanes 32-63, the same columns of the row 4
+// below, so one 64-bit ballot per (register, 32-column block) is the non-zero
+// mask of two rows.  Almost all of the work is scalar: an all-zero block is
+// skipped on a uniform branch, slot = mbcnt(mask) + running count of the row
+// (the running counts are SGPR popcounts), per-row counts are parked in one
+// VGPR (lane i = row i), and only the non-zeros are rounded and stored.
+//
+// A value is a non-zero iff its stored (dtype-rounded) value is: for bf16,
+// round-to-nearest-even of a positive fp32 u is non-zero iff bits(u) >= 0x8001
+// (below that the value rounds to +0), so one signed integer compare on the
+// fp32 bits decides it (negative values and -0 have the sign bit set).
+//
+// The records of 32 rows at a time are assembled in this wave's LDS scratch
+// (zeroed first, so unused slots need no stores) and leave with 16-byte
+// stores.  wlds: pack_scratch_bytes(C, sizeof(dtype)) bytes, 16-byte aligned.
+template <class E, int MB, int KWN, bool DBG>
+__device__ __forceinline__ void pack_epilogue(const PackArgs& p, const f32x16_t (&acc)[MB][KWN], int64_t wrow0,
+                                              int b, char* wlds, uint32_t& ovf, uint32_t& nnz) {
+  constexpr int kTn = 32 * KWN;
+  constexpr int kNzMin = E::kBytes == 2 ? 0x8001 : 1;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, li = lane & 31;
-  const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
+  const int n_t = p.F / kTn;
   const int C = p.C;
-  uint32_t ovf = 0, nnz = 0;
-
+  const int idx_bytes = C, val_bytes = C * E::kBytes;
+  uint8_t* l_idx = reinterpret_cast<uint8_t*>(wlds);
+  char* l_val = wlds + 32 * idx_bytes;
+  const int rec_words = 32 * (idx_bytes + val_bytes) / 4;
+  // copy pieces: 16 bytes when every record is a multiple of 16 bytes, else 4, else 1
+  const int piece = (C % 16) == 0 ? 16 : ((C % 4) == 0 ? 4 : 1);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
+    for (int i = lane; i < rec_words; i += 64) reinterpret_cast<uint32_t*>(wlds)[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t row0 = wrow0 + mb * 32;
+    int cnt_v = 0;  // lane i < 32: count of row row0 + i
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = wrow0 + mb * 32 + acc_row(r, lane);
-      const bool valid = row < p.T;
-      uint32_t bits[kWN];
-      uint32_t mh[kWN];
-      bool nz[kWN];
+      const int ra = 8 * (r >> 2) + (r & 3);  // row of lanes 0-31; lanes 32-63 hold row ra + 4
+      const int rr = ra + 4 * half;
+      int pre_a = 0, pre_b = 0;
 #pragma unroll
-      for (int nb = 0; nb < kWN; ++nb) {
-        const float g = acc.c[mb][nb][r];
-        const Rounded<E> a = round_store<E>(g > 0.f ? g : 0.f);
-        bits[nb] = a.bits;
-        nz[nb] = a.bits != 0u;
-        const uint64_t m = __ballot(nz[nb]);
-        mh[nb] = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
-      }
-      if (!valid) continue;
-      const int64_t rt = row * n_t + b;  // (row, tile) record index
-      int pre = 0;
-#pragma unroll
-      for (int nb = 0; nb < kWN; ++nb) {
-        if (nz[nb]) {
-          const int s = pre + __popc(mh[nb] & ((1u << li) - 1u));
-          if (s < C) {
-            p.idx[rt * C + s] = static_cast<uint8_t>(nb * 32 + li);
-            store_bits<E>(p.val, rt * C + s, bits[nb]);
+      for (int nb = 0; nb < KWN; ++nb) {
+        const uint32_t u = __float_as_uint(acc[mb][nb][r]);
+        const bool nz = static_cast<int>(u) >= kNzMin;
+        if constexpr (DBG) {
+          const int64_t row = row0 + rr;
+          if (row < p.T)
+            store_bits<E>(p.gate_dbg, row * p.F + static_cast<int64_t>(b) * kTn + nb * 32 + li,
+                          nz ? round_store<E>(__uint_as_float(u)).bits : 0u);
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(nz);
+        if (m != 0) {
+          const uint32_t mlo = static_cast<uint32_t>(m), mhi = static_cast<uint32_t>(m >> 32);
+          const int plo = __popc(mlo), phi = __popc(mhi);
+          const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u)));
+          const int s = below + (half ? pre_b - plo : pre_a);
+          if (nz && s < C) {
+            l_idx[rr * idx_bytes + s] = static_cast<uint8_t>(nb * 32 + li);
+            const uint32_t bits = round_store<E>(__uint_as_float(u)).bits;
+            if constexpr (E::kBytes == 2)
+              reinterpret_cast<uint16_t*>(l_val + rr * val_bytes)[s] = static_cast<uint16_t>(bits);
+            else
+              reinterpret_cast<uint32_t*>(l_val + rr * val_bytes)[s] = bits;
           }
-        }
-        pre += __popc(mh[nb]);
-      }
-      for (int s = li; s < C; s += 32) {
-        if (s >= pre) {
-          p.idx[rt * C + s] = 0;
-          store_bits<E>(p.val, rt * C + s, 0u);
+          pre_a += plo;
+          pre_b += phi;
         }
       }
-      if (li == 0) {
-        p.count[rt] = pre;
-        ovf += pre > C ? 1u : 0u;
-        nnz += static_cast<uint32_t>(pre);
+      cnt_v = lane == ra ? pre_a : (lane == ra + 4 ? pre_b : cnt_v);
+      if (row0 + ra < p.T) {
+        ovf += pre_a > C ? 1u : 0u;
+        nnz += static_cast<uint32_t>(pre_a);
       }
-      if (p.gate_dbg) {
-#pragma unroll
-        for (int nb = 0; nb < kWN; ++nb)
-          store_bits<E>(p.gate_dbg, row * p.F + static_cast<int64_t>(b) * BN + nb * 32 + li, bits[nb]);
+      if (row0 + ra + 4 < p.T) {
+        ovf += pre_b > C ? 1u : 0u;
+        nnz += static_cast<uint32_t>(pre_b);
       }
     }
-  }
-  if (p.stats) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      ovf += __shfl_xor(ovf, o);
-      nnz += __shfl_xor(nnz, o);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // write the 32 records out: counts, then index and value pieces
+    if (lane < 32 && row0 + lane < p.T) p.count[(row0 + lane) * n_t + b] = cnt_v;
+    const int ip = idx_bytes / piece, vp = val_bytes / piece;  // pieces per row
+    for (int w = lane; w < 32 * (ip + vp); w += 64) {
+      const int rw = w / (ip + vp), k = w - rw * (ip + vp);
+      const int64_t row = row0 + rw;
+      if (row >= p.T) continue;
+      const int64_t rt = row * n_t + b;
+      const char* src;
+      char* dst;
+      if (k < ip) {
+        src = reinterpret_cast<const char*>(l_idx) + rw * idx_bytes + k * piece;
+        dst = reinterpret_cast<char*>(p.idx) + rt * idx_bytes + k * piece;
+      } else {
+        src = l_val + rw * val_bytes + (k - ip) * piece;
+        dst = static_cast<char*>(p.val) + rt * val_bytes + (k - ip) * piece;
+      }
+      if (piece == 16)
+        *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+      else if (piece == 4)
+        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+      else
+        *dst = *src;
     }
-    if (lane == 0) {
-      if (ovf) atomicAdd(p.stats + 0, static_cast<unsigned long long>(ovf));
-      if (nnz) atomicAdd(p.stats + 1, static_cast<unsigned long long>(nnz));
-    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-template <class E, int BN>
-static hipError_t launch_pack_t(const PackArgs& a, hipStream_t s) {
-  dim3 grid(a.F / BN, static_cast<unsigned>((a.T + kBM - 1) / kBM));
-  const size_t lds = (kBM + BN) * 128;
-  hipLaunchKernelGGL((gate_pack_kernel<E, BN>), grid, dim3(kThreads), lds, s, a);
+// Bytes of LDS scratch one wave's epilogue needs.
+__host__ __device__ constexpr int pack_scratch_bytes(int C, int eb) { return ((32 * C * (1 + eb)) + 15) & ~15; }
+
+// ovf / nnz are wave-uniform (they are built from ballot popcounts), so lane 0
+// publishes the wave's totals.
+__device__ __forceinline__ void pack_stats(const PackArgs& p, uint32_t ovf, uint32_t nnz) {
+  if (!p.stats) return;
+  if ((threadIdx.x & 63) == 0) {
+    if (ovf) atomicAdd(p.stats + 0, static_cast<unsigned long long>(ovf));
+    if (nnz) atomicAdd(p.stats + 1, static_cast<unsigned long long>(nnz));
+  }
+}
+
+// T_n = 128: 256 x 256 workgroup tile (two TwELL tiles); wave w owns rows
+// [128*(w/2), +128) and TwELL tile 2*nt + (w%2).
+template <class E, bool DBG>
+__global__ __launch_bounds__(256, 1) void gate_pack256_kernel(PackArgs p) {
+  extern __shared__ __align__(16) char lds[];
+  const int n_mt = static_cast<int>((p.T + kT256 - 1) / kT256);
+  const int n_nt = (p.F + kT256 - 1) / kT256;
+  int mt, nt;
+  tile_coords_256(n_mt, n_nt, mt, nt);
+  const int64_t m0 = static_cast<int64_t>(mt) * kT256;
+  const int64_t n0 = static_cast<int64_t>(nt) * kT256;
+  DirectRows<E> la, lb;
+  la.init(p.x, p.d, m0, p.T, nullptr);
+  lb.init(p.w_gate_t, p.d, n0, p.F, nullptr);
+  Acc256 acc;
+  gemm256_mainloop<E>(la, lb, p.d / (128 / E::kBytes), lds, acc);
+  const int wave = threadIdx.x >> 6;
+  const int b = static_cast<int>((n0 >> 7) + (wave & 1));
+  uint32_t ovf = 0, nnz = 0;
+  __syncthreads();  // every wave is done with the operand stages: reuse them as epilogue scratch
+  char* wlds = lds + wave * pack_scratch_bytes(p.C, E::kBytes);
+  if (b < p.F / 128) pack_epilogue<E, 4, 4, DBG>(p, acc.c, m0 + (wave >> 1) * 128, b, wlds, ovf, nnz);
+  pack_stats(p, ovf, nnz);
+}
+
+// T_n = 64: 256 x 64 workgroup tile (one TwELL tile); wave w owns rows [64w, +64).
+template <class E, bool DBG>
+__global__ __launch_bounds__(kThreads, 2) void gate_pack64_kernel(PackArgs p) {
+  extern __shared__ __align__(16) char lds[];
+  const int b = blockIdx.x;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
+  KRowLoader<E, kBM> la;
+  KRowLoader<E, 64> lb;
+  la.init(p.x, p.d, m0, p.T, nullptr);
+  lb.init(p.w_gate_t, p.d, static_cast<int64_t>(b) * 64, p.F, nullptr);
+  Acc<64> acc;
+  gemm_mainloop<E, 64>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
+  uint32_t ovf = 0, nnz = 0;
+  __syncthreads();
+  char* wlds = lds + (threadIdx.x >> 6) * pack_scratch_bytes(p.C, E::kBytes);
+  pack_epilogue<E, 2, 2, DBG>(p, acc.c, m0 + (threadIdx.x >> 6) * 64, b, wlds, ovf, nnz);
+  pack_stats(p, ovf, nnz);
+}
+
+template <class E, bool DBG>
+static hipError_t launch_pack256_t(const PackArgs& a, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack256_kernel<E, DBG>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds256);
+  if (attr != hipSuccess) return attr;
+  const unsigned n_mt = static_cast<unsigned>((a.T + kT256 - 1) / kT256);
+  const unsigned n_nt = static_cast<unsigned>((a.F + kT256 - 1) / kT256);
+  hipLaunchKernelGGL((gate_pack256_kernel<E, DBG>), dim3(n_mt * n_nt), dim3(256), kLds256, s, a);
   return hipGetLastError();
 }
 
+template <class E, bool DBG>
+static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
+  dim3 grid(a.F / 64, static_cast<unsigned>((a.T + kBM - 1) / kBM));
+  const size_t lds = std::max<size_t>((kBM + 64) * 128, 4 * pack_scratch_bytes(a.C, E::kBytes));
+  hipLaunchKernelGGL((gate_pack64_kernel<E, DBG>), grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_pack_e(const PackArgs& a, hipStream_t s) {
+  const bool dbg = a.gate_dbg != nullptr;
+  if (a.tile_n == 128) return dbg ? launch_pack256_t<E, true>(a, s) : launch_pack256_t<E, false>(a, s);
+  return dbg ? launch_pack64_t<E, true>(a, s) : launch_pack64_t<E, false>(a, s);
+}
+
 hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s) {
-  if (dtype == 1) return a.tile_n == 128 ? launch_pack_t<EBf16, 128>(a, s) : launch_pack_t<EBf16, 64>(a, s);
-  return a.tile_n == 128 ? launch_pack_t<EF32, 128>(a, s) : launch_pack_t<EF32, 64>(a, s);
+  return dtype == 1 ? launch_pack_e<EBf16>(a, s) : launch_pack_e<EF32>(a, s);
 }
 
 }  // namespace twell

@@ -36,7 +36,7 @@ twell_status check_desc(const twell_desc* d) {
 
 twell_status check_act(const twell_act& a) {
   if (!a.count || !a.idx || !a.val) return TWELL_EINVAL;
-  if (!aligned4(a.count) || !aligned4(a.val)) return TWELL_EINVAL;
+  if (!aligned16(a.count) || !aligned16(a.idx) || !aligned16(a.val)) return TWELL_EINVAL;
   return TWELL_OK;
 }
 
