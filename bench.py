@@ -43,7 +43,24 @@ def parse():
     ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
     ap.add_argument("--train-config", type=int, default=4, help="workload of the training-step measurement")
     ap.add_argument("--max-dense-rows", type=int, default=1024)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run one plain fp32 negation of this many MiB (reads and writes "
+                         "exactly that much): the reference dispatch that scales rocprofv3 FETCH_SIZE / "
+                         "WRITE_SIZE to bytes")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --calib-copy-mib run into profiles/traffic_<kernel>.json")
+    ap.add_argument("--traffic-command", default="", help="command line recorded with --traffic-summary")
     return ap.parse_args()
+
+
+# sources whose change invalidates a kernel's measured counters
+KERNEL_SOURCES = {
+    "gate_pack": ["k_gate_pack.hip", "gemm256.hpp", "gemm_core.hpp", "common.hpp"],
+    "fused_updown": ["k_fused_updown.hip", "common.hpp"],
+}
+# substrings of the dispatch names of each kernel
+KERNEL_NAMES = {"gate_pack": "gate_pack", "fused_updown": "fused_updown", "calib_copy": "neg_kernel"}
 
 
 def kernel_source_hash(files):
@@ -65,6 +82,52 @@ def measured_traffic(kernel: str, src_hash: str, per_launch_units: float):
     if t.get("source_hash") != src_hash:
         return None
     return t.get("bytes_per_launch")
+
+
+def _pmc_per_dispatch(path: str, counter: str):
+    """{kernel key: mean counter value per dispatch} from a counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            for key, pat in KERNEL_NAMES.items():
+                if pat in row["Kernel_Name"]:
+                    vals.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
+                    vals[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: (sum(d.values()) / len(d), len(d)) for k, d in vals.items()}
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters
+    read for the calibration copy of known size, and store bytes per launch."""
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    if "calib_copy" not in fetch or "calib_copy" not in write:
+        raise SystemExit("no calibration copy dispatch in the counter files (run bench.py with --calib-copy-mib)")
+    known = calib_mib * 1024 * 1024
+    f_fac = known / (fetch["calib_copy"][0] * 1024)
+    w_fac = known / (write["calib_copy"][0] * 1024)
+    out = {}
+    for key in KERNEL_SOURCES:
+        if key not in fetch or key not in write:
+            continue
+        rb = fetch[key][0] * 1024 * f_fac
+        wb = write[key][0] * 1024 * w_fac
+        rec = {"kernel": key, "source_hash": kernel_source_hash(KERNEL_SOURCES[key]),
+               "fetch_kib_per_dispatch": round(fetch[key][0], 1), "write_kib_per_dispatch": round(write[key][0], 1),
+               "dispatches": [fetch[key][1], write[key][1]],
+               "calib_copy_bytes": known, "calib_fetch_kib": round(fetch["calib_copy"][0], 1),
+               "calib_write_kib": round(write["calib_copy"][0], 1),
+               "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+               "read_bytes_per_launch": int(rb), "write_bytes_per_launch": int(wb),
+               "bytes_per_launch": int(rb + wb), "command": command}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        out[key] = rec
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -140,6 +203,9 @@ def train_step(T, W, args, steps, warmup):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.calib_copy_mib, args.traffic_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
@@ -185,6 +251,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calib_copy_mib > 0:
+        src_c = torch.ones(args.calib_copy_mib * (1 << 18), dtype=torch.float32, device="cuda")
+        dst_c = torch.empty_like(src_c)
+        torch.cuda.synchronize()
+        torch.neg(src_c, out=dst_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -232,8 +305,7 @@ def main():
     touched = 1.0 - (1.0 - density) ** w.T
     fused_bytes = 2 * w.T * w.d_model * eb + twell_bytes + 2 * touched * w.d_ff * w.d_model * eb
     gathered_bytes = nnz * 2 * w.d_model * eb
-    src = {"gate_pack": kernel_source_hash(["k_gate_pack.hip", "gemm_core.hpp", "common.hpp"]),
-           "fused_updown": kernel_source_hash(["k_fused_updown.hip", "common.hpp"])}
+    src = {k: kernel_source_hash(f) for k, f in KERNEL_SOURCES.items()}
     if pack_ms >= fused_ms:
         ach = gate_flop / (pack_ms * 1e-3) / 1e12
         roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(ach, 1), "peak": peak_mm,
