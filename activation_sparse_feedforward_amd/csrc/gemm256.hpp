@@ -48,16 +48,21 @@ template <class E>
 struct DirectRows {
   const char* ptr[8];  // this lane's source for rounds 0..7 at K slice 0
 
-  // tile row r comes from matrix row row_of(r) = (table ? table[row0 + r] : row0 + r),
-  // with row0 + r clamped to nvalid - 1 (nvalid >= 1).
+  // tile row r comes from matrix row row_of(r) = (table ? table[row0 + p(r)] : row0 + p(r)),
+  // with row0 + p(r) clamped to nvalid - 1 (nvalid >= 1).  p is the identity, or
+  // with lane_cols the permutation inside each 128-row half that puts matrix
+  // row 4*l + j at tile row 32*j + l (l < 32, j < 4): used on the B operand,
+  // it makes lane l of the wave's accumulator block j hold output column
+  // 4*l + j, so every lane holds 4 consecutive columns of its rows.
   __device__ __forceinline__ void init(const void* base, int64_t ld, int64_t row0, int64_t nvalid,
-                                       const int32_t* table) {
+                                       const int32_t* table, bool lane_cols = false) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int pc = lane & 7;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int r = q * 32 + wave * 8 + (lane >> 3);
-      int64_t gr = row0 + r;
+      const int rp = lane_cols ? ((r & 128) | ((r & 31) << 2) | ((r >> 5) & 3)) : r;
+      int64_t gr = row0 + rp;
       gr = gr < nvalid ? gr : nvalid - 1;
       if (table) gr = table[gr];
       const int c = pc ^ lds_swz(r);

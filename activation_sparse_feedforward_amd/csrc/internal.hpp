@@ -62,8 +62,9 @@ struct GateUpArgs {
 
 // y[row(m), :] = h[m, :] . w_down  for m < n_rows (row(m) as above, scatter).
 struct DownArgs {
-  const void* h;       // [M x F]
-  const void* w_down;  // [F x d]
+  const void* h;         // [M x F]
+  const void* w_down;    // [F x d]
+  const void* w_down_t;  // [d x F] (launch_dense256: written there from w_down first)
   void* y;             // [T x d]
   const int32_t* rows;
   const int32_t* n_rows_dev;
@@ -108,6 +109,9 @@ hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fused_updown(const FusedArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
+// Full dense FFN on the 256 x 256 core: transpose w_down into dn.w_down_t,
+// gateup256 (all M rows), down256.  dn.h must be g.h.
+hipError_t launch_dense256(const GateUpArgs& g, const DownArgs& dn, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_bwd_sparse(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_bwd_dense(const BwdArgs& a, int dtype, hipStream_t s);

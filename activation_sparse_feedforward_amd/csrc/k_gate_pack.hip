@@ -138,8 +138,149 @@ __device__ __forceinline__ void pack_epilogue(const PackArgs& p, const f32x16_t 
   }
 }
 
+// Lane-column variant for a wave tile of 128 rows x one TwELL tile of 128
+// columns whose B operand was loaded with DirectRows' lane_cols permutation:
+// lane l of accumulator block j holds tile column 4*l + j, so each lane holds 4
+// consecutive columns of a row, and a row's ascending column order is lane
+// order, then j.  One register index r covers 2 rows x 128 columns (lanes 0-31:
+// row ra, lanes 32-63: row ra + 4).  A non-zero's slot is the exclusive prefix,
+// over the lanes of its half, of the per-lane non-zero counts c (0..4), plus
+// its rank inside the lane; the prefix is built from the ballots of c >= k
+// (k = 1..4; prefix(c) = sum_k prefix([c >= k])), where lanes with two or more
+// non-zeros are rare enough to sit behind a uniform branch.  Records are
+// assembled in LDS exactly as in pack_epilogue.  The statistics (overflowing
+// tiles, non-zeros) are computed from the final counts, and only when asked.
+// Row counts are parked in LDS as they are produced (lanes 0 and 32 write the
+// two rows of a register), which keeps 32 scalar counts from piling up in SGPRs.
+// kC > 0 fixes C at compile time (record offsets become immediates); 0 reads p.C.
+// wlds: pack_lc_scratch_bytes(C, sizeof(dtype)) bytes, 16-byte aligned.
+template <class E, bool DBG, int kC>
+__device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16_t (&acc)[4][4], int64_t wrow0,
+                                                 int b, char* wlds, uint32_t& ovf, uint32_t& nnz) {
+  constexpr int kNzMin = E::kBytes == 2 ? 0x8001 : 1;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, li = lane & 31;
+  const int n_t = p.F / 128;
+  const int C = kC > 0 ? kC : p.C;
+  const int idx_bytes = C, val_bytes = C * E::kBytes;
+  uint8_t* l_idx = reinterpret_cast<uint8_t*>(wlds);
+  char* l_val = wlds + 32 * idx_bytes;
+  const int rec_words = 32 * (idx_bytes + val_bytes) / 4;
+  int* l_cnt = reinterpret_cast<int*>(wlds + ((32 * (idx_bytes + val_bytes) + 15) & ~15));
+  const int piece = (C % 16) == 0 ? 16 : ((C % 4) == 0 ? 4 : 1);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    for (int i = lane; i < rec_words; i += 64) reinterpret_cast<uint32_t*>(wlds)[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t row0 = wrow0 + mb * 32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ra = 8 * (r >> 2) + (r & 3);
+      const int rr = ra + 4 * half;
+      uint32_t u[4];
+      int bits = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u[j] = __float_as_uint(acc[mb][j][r]);
+        bits |= (static_cast<int>(u[j]) >= kNzMin ? 1 : 0) << j;
+      }
+      if constexpr (DBG) {
+        const int64_t row = row0 + rr;
+        if (row < p.T)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            store_bits<E>(p.gate_dbg, row * p.F + static_cast<int64_t>(b) * 128 + 4 * li + j,
+                          (bits >> j) & 1 ? round_store<E>(__uint_as_float(u[j])).bits : 0u);
+      }
+      const uint64_t m1 = __builtin_amdgcn_ballot_w64(bits != 0);
+      int pre_a = 0, pre_b = 0;
+      if (m1 != 0) {
+        const int c = __popc(bits);
+        const uint32_t lo1 = static_cast<uint32_t>(m1), hi1 = static_cast<uint32_t>(m1 >> 32);
+        pre_a = __popc(lo1);
+        pre_b = __popc(hi1);
+        int excl = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi1, __builtin_amdgcn_mbcnt_lo(lo1, 0u))) -
+                   (half ? pre_a : 0);
+        const uint64_t m2 = __builtin_amdgcn_ballot_w64(c >= 2);
+        if (m2 != 0) {
+#pragma unroll
+          for (int k = 2; k <= 4; ++k) {
+            const uint64_t mk = __builtin_amdgcn_ballot_w64(c >= k);
+            const uint32_t lo = static_cast<uint32_t>(mk), hi = static_cast<uint32_t>(mk >> 32);
+            const int plo = __popc(lo);
+            excl += static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))) -
+                    (half ? plo : 0);
+            pre_a += plo;
+            pre_b += __popc(hi);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if ((bits >> j) & 1) {
+            const int s = excl + __popc(bits & ((1 << j) - 1));
+            if (s < C) {
+              l_idx[rr * idx_bytes + s] = static_cast<uint8_t>(4 * li + j);
+              const uint32_t vb = round_store<E>(__uint_as_float(u[j])).bits;
+              if constexpr (E::kBytes == 2)
+                reinterpret_cast<uint16_t*>(l_val + rr * val_bytes)[s] = static_cast<uint16_t>(vb);
+              else
+                reinterpret_cast<uint32_t*>(l_val + rr * val_bytes)[s] = vb;
+            }
+          }
+        }
+      }
+      if (li == 0) l_cnt[rr] = half ? pre_b : pre_a;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int cnt_v = l_cnt[li];  // lane i < 32: count of row row0 + i
+    const bool row_ok = lane < 32 && row0 + lane < p.T;
+    if (p.stats) {
+      const int cv = row_ok ? cnt_v : 0;
+      ovf += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(cv > C)));
+      int sum = cv;
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+      nnz += static_cast<uint32_t>(__shfl(sum, 0));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (row_ok) p.count[(row0 + lane) * n_t + b] = cnt_v;
+    const int ip = idx_bytes / piece, vp = val_bytes / piece;
+    for (int w = lane; w < 32 * (ip + vp); w += 64) {
+      const int rw = w / (ip + vp), k = w - rw * (ip + vp);
+      const int64_t row = row0 + rw;
+      if (row >= p.T) continue;
+      const int64_t rt = row * n_t + b;
+      const char* src;
+      char* dst;
+      if (k < ip) {
+        src = reinterpret_cast<const char*>(l_idx) + rw * idx_bytes + k * piece;
+        dst = reinterpret_cast<char*>(p.idx) + rt * idx_bytes + k * piece;
+      } else {
+        src = l_val + rw * val_bytes + (k - ip) * piece;
+        dst = static_cast<char*>(p.val) + rt * val_bytes + (k - ip) * piece;
+      }
+      if (piece == 16)
+        *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+      else if (piece == 4)
+        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+      else
+        *dst = *src;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // Bytes of LDS scratch one wave's epilogue needs.
 __host__ __device__ constexpr int pack_scratch_bytes(int C, int eb) { return ((32 * C * (1 + eb)) + 15) & ~15; }
+__host__ __device__ constexpr int pack_lc_scratch_bytes(int C, int eb) { return pack_scratch_bytes(C, eb) + 128; }
 
 // ovf / nnz are wave-uniform (they are built from ballot popcounts), so lane 0
 // publishes the wave's totals.
@@ -153,7 +294,7 @@ __device__ __forceinline__ void pack_stats(const PackArgs& p, uint32_t ovf, uint
 
 // T_n = 128: 256 x 256 workgroup tile (two TwELL tiles); wave w owns rows
 // [128*(w/2), +128) and TwELL tile 2*nt + (w%2).
-template <class E, bool DBG>
+template <class E, bool DBG, int kC>
 __global__ __launch_bounds__(256, 1) void gate_pack256_kernel(PackArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int n_mt = static_cast<int>((p.T + kT256 - 1) / kT256);
@@ -164,15 +305,15 @@ __global__ __launch_bounds__(256, 1) void gate_pack256_kernel(PackArgs p) {
   const int64_t n0 = static_cast<int64_t>(nt) * kT256;
   DirectRows<E> la, lb;
   la.init(p.x, p.d, m0, p.T, nullptr);
-  lb.init(p.w_gate_t, p.d, n0, p.F, nullptr);
+  lb.init(p.w_gate_t, p.d, n0, p.F, nullptr, /*lane_cols=*/true);
   Acc256 acc;
   gemm256_mainloop<E>(la, lb, p.d / (128 / E::kBytes), lds, acc);
   const int wave = threadIdx.x >> 6;
   const int b = static_cast<int>((n0 >> 7) + (wave & 1));
   uint32_t ovf = 0, nnz = 0;
   __syncthreads();  // every wave is done with the operand stages: reuse them as epilogue scratch
-  char* wlds = lds + wave * pack_scratch_bytes(p.C, E::kBytes);
-  if (b < p.F / 128) pack_epilogue<E, 4, 4, DBG>(p, acc.c, m0 + (wave >> 1) * 128, b, wlds, ovf, nnz);
+  char* wlds = lds + wave * pack_lc_scratch_bytes(kC > 0 ? kC : p.C, E::kBytes);
+  if (b < p.F / 128) pack_epilogue_lc<E, DBG, kC>(p, acc.c, m0 + (wave >> 1) * 128, b, wlds, ovf, nnz);
   pack_stats(p, ovf, nnz);
 }
 
@@ -195,15 +336,23 @@ __global__ __launch_bounds__(kThreads, 2) void gate_pack64_kernel(PackArgs p) {
   pack_stats(p, ovf, nnz);
 }
 
-template <class E, bool DBG>
-static hipError_t launch_pack256_t(const PackArgs& a, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack256_kernel<E, DBG>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds256);
+template <class E, bool DBG, int kC>
+static hipError_t launch_pack256_c(const PackArgs& a, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gate_pack256_kernel<E, DBG, kC>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      kLds256);
   if (attr != hipSuccess) return attr;
   const unsigned n_mt = static_cast<unsigned>((a.T + kT256 - 1) / kT256);
   const unsigned n_nt = static_cast<unsigned>((a.F + kT256 - 1) / kT256);
-  hipLaunchKernelGGL((gate_pack256_kernel<E, DBG>), dim3(n_mt * n_nt), dim3(256), kLds256, s, a);
+  hipLaunchKernelGGL((gate_pack256_kernel<E, DBG, kC>), dim3(n_mt * n_nt), dim3(256), kLds256, s, a);
   return hipGetLastError();
+}
+
+template <class E, bool DBG>
+static hipError_t launch_pack256_t(const PackArgs& a, hipStream_t s) {
+  // 4 waves' epilogue scratch must fit in the operand stages it reuses
+  static_assert(4 * pack_lc_scratch_bytes(128, 4) <= kLds256, "pack scratch exceeds the GEMM stages");
+  return a.C == 16 ? launch_pack256_c<E, DBG, 16>(a, s) : launch_pack256_c<E, DBG, 0>(a, s);
 }
 
 template <class E, bool DBG>

@@ -106,7 +106,8 @@ twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_size
   out->count = T * n_t * 4;
   out->idx = T * n_t * C;
   out->val = T * n_t * C * eb;
-  out->ws_dense_fwd = T * static_cast<size_t>(d->d_ff) * eb;
+  out->ws_dense_fwd = align256(T * static_cast<size_t>(d->d_ff) * eb) +
+                      static_cast<size_t>(d->d_model) * static_cast<size_t>(d->d_ff) * eb;
   const HybridWs hw = hybrid_ws(d, max_dense_rows);
   out->ws_hybrid = hw.total;
   out->ws_bwd = bwd_ws(d, max_dense_rows).total;
@@ -326,17 +327,17 @@ twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void*
   g.M = d->T;
   g.d = d->d_model;
   g.F = d->d_ff;
-  TWELL_TRY(from_hip(twell::launch_gateup(g, d->dtype, s)));
   twell::DownArgs dn{};
   dn.h = ws;
   dn.w_down = w_down;
+  dn.w_down_t = static_cast<char*>(ws) + align256(static_cast<size_t>(d->T) * d->d_ff * elem_bytes(d));
   dn.y = y;
   dn.rows = nullptr;
   dn.n_rows_dev = nullptr;
   dn.M = d->T;
   dn.d = d->d_model;
   dn.F = d->d_ff;
-  return from_hip(twell::launch_down(dn, d->dtype, s));
+  return from_hip(twell::launch_dense256(g, dn, d->dtype, s));
 }
 
 const char* twell_status_str(twell_status s) {

@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
     ap.add_argument("--train-config", type=int, default=4, help="workload of the training-step measurement")
     ap.add_argument("--max-dense-rows", type=int, default=1024)
+    ap.add_argument("--cold-iters", type=int, default=20,
+                    help="iterations of the cold-cache timing (a 1 GiB write before each; 0 = skip)")
+    ap.add_argument("--no-hipblaslt", action="store_true", help="skip the torch.matmul dense sanity point")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one plain fp32 negation of this many MiB (reads and writes "
                          "exactly that much): the reference dispatch that scales rocprofv3 FETCH_SIZE / "
@@ -151,6 +154,57 @@ def cpu_baseline(inp, budget_s: float):
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} tokens of the timed workload, oracle dense float64 forward "
                       f"(NumPy matmul), {dt:.1f} s"}
+
+
+def _pct(v):
+    import numpy as np
+    return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+            "p90": round(float(np.percentile(v, 90)), 4)}
+
+
+def cold_timing(phases, iters, stream):
+    """Per-phase times with L2 and MALL flushed before every iteration: a 1 GiB
+    buffer is written (and the write completed) before each timed pass.
+    phases: list of (name, callable)."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {n: [] for n, _ in phases}
+    out["total"] = []
+    for k in range(iters):
+        flush.fill_(float(k))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        ev[0].record(stream)
+        for i, (_, fn) in enumerate(phases):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i, (n, _) in enumerate(phases):
+            out[n].append(ev[i].elapsed_time(ev[i + 1]))
+        out["total"].append(ev[0].elapsed_time(ev[-1]))
+    del flush
+    return {n: _pct(v) for n, v in out.items()}
+
+
+def hipblaslt_dense(x, wg, wu, wd, steps, warmup, stream):
+    """The dense FFN through torch.matmul (hipBLASLt GEMMs, torch elementwise),
+    as a sanity point for the library's own dense path."""
+    import torch
+
+    def run():
+        g = torch.matmul(x, wg.t())
+        u = torch.matmul(x, wu.t())
+        return torch.matmul(torch.relu(g) * u, wd)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def train_step(T, W, args, steps, warmup):
@@ -294,7 +348,21 @@ def main():
         flops = 6.0 * w.T * w.d_model * w.d_ff
         dense = {"ms_per_step": round(dense_ms, 4), "tokens_per_s": round(w.T / dense_ms * 1e3, 1),
                  "tflops": round(flops / dense_ms / 1e9, 1)}
+        if args.cold_iters > 0:
+            dense["cold_ms"] = cold_timing(
+                [("dense", lambda: T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, yd, ws, stream=stream))],
+                args.cold_iters, stream)["dense"]
         del ws, yd
+        if not args.no_hipblaslt and w.dtype == "bf16":
+            hb = hipblaslt_dense(x, wg, wu, wd, K, args.warmup, stream)
+            dense["torch_matmul_sanity"] = {"ms_per_step": round(hb, 4), "tflops": round(flops / hb / 1e9, 1)}
+            torch.cuda.empty_cache()
+
+    cold = None
+    if args.cold_iters > 0:
+        cold = cold_timing([("gate_pack", lambda: T.twell_pack(desc, x, wg, act, stream=stream)),
+                            ("fused_updown", lambda: T.twell_ffn_fwd(desc, x, act, wu, wd, y, stream=stream))],
+                           args.cold_iters, stream)
 
     # roofline of the dominant kernel
     peak_mm = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -342,6 +410,9 @@ def main():
                          "gathered_bytes": int(gathered_bytes), "required_bytes": int(fused_bytes)},
         "dense_ffn": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 3) if dense else None,
+        "cold_ms": cold,
+        "speedup_vs_dense_cold": (round(dense["cold_ms"]["median"] / cold["total"]["median"], 3)
+                                  if dense and cold and "cold_ms" in dense else None),
     }
     if not args.no_train:
         del act, y

@@ -98,7 +98,7 @@ typedef struct {
   size_t count;        /* T * n_t * 4                                        */
   size_t idx;          /* T * n_t * C                                        */
   size_t val;          /* T * n_t * C * sizeof(dtype)                        */
-  size_t ws_dense_fwd; /* workspace of twell_dense_ffn_fwd: h [T x d_ff]      */
+  size_t ws_dense_fwd; /* twell_dense_ffn_fwd: h [T x d_ff] + W_down^T         */
   size_t ws_hybrid;    /* workspace of twell_ffn_fwd_hybrid (max_dense_rows)  */
   size_t ws_bwd;       /* workspace of twell_ffn_bwd (max_dense_rows)         */
 } twell_sizes_t;
@@ -172,9 +172,10 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
 /* The library's own dense MFMA FFN, the baseline the sparse path is compared with.
  * [P2 §Problema: GPUs are built for dense matrix products; the sparse path must
  * beat the dense one.]
- * Kernel 1: g = x w_gate, u = x w_up in one GEMM, epilogue h = ReLU(g) * u
+ * Kernel 1: W_down^T [d_model x d_ff] written into ws (after h, 256-byte aligned);
+ * Kernel 2: g = x w_gate, u = x w_up in one GEMM, epilogue h = ReLU(g) * u
  *           stored to ws as dtype [T x d_ff];
- * Kernel 2: y = h w_down (y overwritten, dtype).
+ * Kernel 3: y = h w_down (y overwritten, dtype).
  * ws must hold twell_sizes().ws_dense_fwd bytes. */
 twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,
                                  const void* w_up_t, const void* w_down, void* y, void* ws,

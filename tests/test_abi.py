@@ -53,7 +53,7 @@ def test_sizes_values():
     assert s["count"] == 16384 * 64 * 4
     assert s["idx"] == 16384 * 64 * 16
     assert s["val"] == 16384 * 64 * 16 * 2
-    assert s["ws_dense_fwd"] == 16384 * 8192 * 2
+    assert s["ws_dense_fwd"] == 16384 * 8192 * 2 + 2048 * 8192 * 2  # h, then W_down^T
     h = T.sizes(T.Desc(16384, 2048, 8192, 128, 16, "bf16"), max_dense_rows=1000)
     assert h["ws_hybrid"] >= 1000 * 8192 * 2 + 64 * 4
     d = T.Desc(16, 512, 1024, 128, 16, "bf16").c()

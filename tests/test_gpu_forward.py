@@ -185,3 +185,21 @@ def test_full_size_sampled_rows(cfg):
     float64 checks on sampled rows (first and last M tiles plus random rows)."""
     w = W.workload(cfg)
     _check_case(w, rows=_sample_rows(w.T, cfg), label=f"full c{cfg}")
+
+
+def test_dense_ffn_full_size_sampled():
+    """The dense FFN in the configuration the benchmark times (2B-class shape,
+    T=16384), checked on sampled rows against the float64 dense FFN."""
+    w = W.workload(3)
+    say(f"[gpu case] dense full c3 T={w.T}")
+    inp = W.make_inputs(w)
+    desc = desc_for(w)
+    x, wg, wu, wd = (dev(inp[k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
+    y = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
+    ws = torch.empty(T.sizes(desc)["ws_dense_fwd"], dtype=torch.uint8, device="cuda")
+    T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, y, ws)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.T, 7)
+    yr = O.ffn_forward(inp["x"][rows], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])["y"]
+    err = np.abs(host64(y)[rows] - yr).max()
+    assert err <= TOL[w.dtype] * np.abs(yr).max(), (err, np.abs(yr).max())
