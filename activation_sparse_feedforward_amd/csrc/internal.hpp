@@ -70,7 +70,19 @@ struct DownArgs {
   const int32_t* n_rows_dev;
   int64_t M;
   int32_t d, F;
+  // split-K (launch_down only): splits > 1 writes fp32 partials part[split][M][d]
+  // and a fixed-order reduction then rounds them into y (deterministic)
+  float* part;
+  int32_t splits;
 };
+// Split-K factor for a skinny GEMM over K (a multiple of slice elements): the
+// largest s in {16, 8, 4, 2, 1} with K / s >= 512 and K / s a multiple of the
+// slice, so that few M tiles still fill the chip.
+inline int split_k_for(int64_t K, int slice_elems) {
+  for (int s = 16; s > 1; s >>= 1)
+    if (K / s >= 512 && (K / slice_elems) % s == 0) return s;
+  return 1;
+}
 
 // Backward of the hybrid-format FFN (sparse rows: k_bwd.hip, dense rows: k_bwd_dense.hip).
 struct BwdArgs {
@@ -102,6 +114,8 @@ struct BwdArgs {
   void* dg_d;           // [cap][F] dtype
   void* du_d;
   void* h_d;
+  float* dx_part;       // [dx_splits][cap][d] fp32 split-K partials of the dense rows' dx
+  int32_t dx_splits;
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -113,6 +127,10 @@ hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
 // gateup256 (all M rows), down256.  dn.h must be g.h.
 hipError_t launch_dense256(const GateUpArgs& g, const DownArgs& dn, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// out[row(m), :] = round(sum_{s < splits} part[s][m][:]) for m < n_rows (n_rows =
+// *n_rows_dev, row(m) = rows[m] or m), summed in ascending s.  d % 4 == 0.
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, const int32_t* n_rows_dev,
+                                const int32_t* rows, void* out, int d, int dtype, hipStream_t s);
 hipError_t launch_bwd_sparse(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_bwd_dense(const BwdArgs& a, int dtype, hipStream_t s);
 

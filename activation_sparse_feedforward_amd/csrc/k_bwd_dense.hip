@@ -100,20 +100,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dx_kernel(BwdArgs p) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   if (m0 >= n) return;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128;
-  const int nk = p.F / KRowLoader<E, kBM>::kSliceElems;
+  // split-K over the neurons: blockIdx.z takes j in [k0, k0 + ks)
+  const int splits = p.dx_splits > 1 ? p.dx_splits : 1;
+  const int64_t ks = p.F / splits, k0 = static_cast<int64_t>(blockIdx.z) * ks;
+  const int nk = static_cast<int>(ks / KRowLoader<E, kBM>::kSliceElems);
   Acc<128> acc;
   {
     KRowLoader<E, kBM> la;
-    la.init(p.dg_d, p.F, m0, n, nullptr);
+    la.init(static_cast<const char*>(p.dg_d) + k0 * E::kBytes, p.F, m0, n, nullptr);
     MNColLoader<E, 128> lb;
-    lb.init(p.w_gate_t, p.d, n0, p.d, p.F);
+    lb.init(static_cast<const char*>(p.w_gate_t) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
     gemm_mainloop<E, 128>(la, lb, nk, lds, acc);
   }
   {
     KRowLoader<E, kBM> la;
-    la.init(p.du_d, p.F, m0, n, nullptr);
+    la.init(static_cast<const char*>(p.du_d) + k0 * E::kBytes, p.F, m0, n, nullptr);
     MNColLoader<E, 128> lb;
-    lb.init(p.w_up_t, p.d, n0, p.d, p.F);
+    lb.init(static_cast<const char*>(p.w_up_t) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
     gemm_mainloop<E, 128>(la, lb, nk, lds, acc, /*accumulate=*/true);
   }
   const int lane = threadIdx.x & 63;
@@ -124,6 +127,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dx_kernel(BwdArgs p) {
     for (int r = 0; r < 16; ++r) {
       const int64_t m = wrow0 + mb * 32 + acc_row(r, lane);
       if (m >= n) continue;
+      if (splits > 1) {
+        float* o = p.dx_part + (static_cast<int64_t>(blockIdx.z) * p.cap + m) * p.d + n0 + (lane & 31);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) o[nb * 32] = acc.c[mb][nb][r];
+        continue;
+      }
       const int64_t row = p.dense_rows[m];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
@@ -175,8 +184,14 @@ static hipError_t launch_bwd_dense_t(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dh_kernel<E>), dim3((a.F + 127) / 128, mrows), dim3(kThreads), lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dx_kernel<E>), dim3(a.d / 128, mrows), dim3(kThreads), lds, s, a);
+  const int splits = a.dx_splits > 1 ? a.dx_splits : 1;
+  hipLaunchKernelGGL((bwd_dx_kernel<E>), dim3(a.d / 128, mrows, splits), dim3(kThreads), lds, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (splits > 1) {
+    e = launch_splitk_reduce(a.dx_part, splits, a.cap, a.n_rows + 1, a.dense_rows, a.dx, a.d,
+                             E::kBytes == 2 ? 1 : 0, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bwd_dw_dense_kernel<E>), dim3(a.d / 128, (a.F + kBM - 1) / kBM, 3), dim3(kThreads), lds, s,
                      a);
   return hipGetLastError();

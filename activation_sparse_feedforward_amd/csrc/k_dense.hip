@@ -70,13 +70,16 @@ __global__ __launch_bounds__(kThreads, 2) void down_kernel(DownArgs p) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   if (m0 >= n_rows) return;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128;
+  // split-K: blockIdx.z takes K rows [k0, k0 + ks) of h's columns / W_down's rows
+  const int splits = p.splits > 1 ? p.splits : 1;
+  const int64_t ks = p.F / splits, k0 = static_cast<int64_t>(blockIdx.z) * ks;
 
   KRowLoader<E, kBM> la;
-  la.init(p.h, p.F, m0, n_rows, nullptr);
+  la.init(static_cast<const char*>(p.h) + k0 * E::kBytes, p.F, m0, n_rows, nullptr);
   MNColLoader<E, 128> lb;
-  lb.init(p.w_down, p.d, n0, p.d, p.F);
+  lb.init(static_cast<const char*>(p.w_down) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
   Acc<128> acc;
-  gemm_mainloop<E, 128>(la, lb, p.F / KRowLoader<E, kBM>::kSliceElems, lds, acc);
+  gemm_mainloop<E, 128>(la, lb, static_cast<int>(ks / KRowLoader<E, kBM>::kSliceElems), lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
@@ -86,12 +89,57 @@ __global__ __launch_bounds__(kThreads, 2) void down_kernel(DownArgs p) {
     for (int r = 0; r < 16; ++r) {
       const int64_t m = wrow0 + mb * 32 + acc_row(r, lane);
       if (m >= n_rows) continue;
+      if (splits > 1) {
+        float* o = p.part + (static_cast<int64_t>(blockIdx.z) * p.M + m) * p.d + n0 + (lane & 31);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) o[nb * 32] = acc.c[mb][nb][r];
+        continue;
+      }
       const int64_t row = p.rows ? static_cast<int64_t>(p.rows[m]) : m;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
         store_bits<E>(p.y, row * p.d + n0 + nb * 32 + (lane & 31), round_store<E>(acc.c[mb][nb][r]).bits);
     }
   }
+}
+
+// Fixed-order sum of split-K partials, rounded and scattered to the output
+// rows; 4 consecutive columns per thread.  Threads past n_rows exit.
+template <class E>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t M,
+                                                            const int32_t* n_rows_dev, const int32_t* rows,
+                                                            void* out, int d) {
+  const int64_t n_rows = n_rows_dev ? static_cast<int64_t>(*n_rows_dev) : M;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t m = i / d;
+  if (m >= n_rows || m >= M) return;
+  const int64_t n = i - m * d;
+  float4 acc = *reinterpret_cast<const float4*>(part + m * d + n);
+  for (int s = 1; s < splits; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (static_cast<int64_t>(s) * M + m) * d + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const int64_t o = (rows ? static_cast<int64_t>(rows[m]) : m) * d + n;
+  store_bits<E>(out, o + 0, round_store<E>(acc.x).bits);
+  store_bits<E>(out, o + 1, round_store<E>(acc.y).bits);
+  store_bits<E>(out, o + 2, round_store<E>(acc.z).bits);
+  store_bits<E>(out, o + 3, round_store<E>(acc.w).bits);
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, const int32_t* n_rows_dev,
+                                const int32_t* rows, void* out, int d, int dtype, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((M * d / 4 + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL((splitk_reduce_kernel<EBf16>), dim3(blocks), dim3(256), 0, s, part, splits, M, n_rows_dev,
+                       rows, out, d);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<EF32>), dim3(blocks), dim3(256), 0, s, part, splits, M, n_rows_dev,
+                       rows, out, d);
+  return hipGetLastError();
 }
 
 // gate|up on the 256 x 256 core: workgroup tile = 256 rows x 128 neurons.  The
@@ -218,9 +266,12 @@ static hipError_t launch_gateup_t(const GateUpArgs& a, hipStream_t s) {
 
 template <class E>
 static hipError_t launch_down_t(const DownArgs& a, hipStream_t s) {
-  dim3 grid(a.d / 128, static_cast<unsigned>((a.M + kBM - 1) / kBM));
+  const int splits = a.splits > 1 ? a.splits : 1;
+  dim3 grid(a.d / 128, static_cast<unsigned>((a.M + kBM - 1) / kBM), splits);
   hipLaunchKernelGGL((down_kernel<E>), grid, dim3(kThreads), (kBM + 128) * 128, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(a.part, splits, a.M, a.n_rows_dev, a.rows, a.y, a.d, E::kBytes == 2 ? 1 : 0, s);
 }
 
 hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s) {

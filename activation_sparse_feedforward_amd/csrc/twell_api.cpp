@@ -49,21 +49,30 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layout of the hybrid forward: router block counts, then the dense
 // rows' hidden activations h [max_dense_rows x d_ff].
+// Split-K factor of the dense rows' GEMMs that reduce over d_ff.
+int dense_splits(const twell_desc* d) { return twell::split_k_for(d->d_ff, 128 / elem_bytes(d)); }
+
+// Workspace layout of the hybrid forward: router block counts, the dense rows'
+// hidden activations h [max_dense_rows x d_ff], and the split-K partials of
+// their down GEMM [splits x max_dense_rows x d_model] fp32 (splits > 1 only).
 struct HybridWs {
-  size_t block_dense, h, total;
+  size_t block_dense, h, part, total;
 };
 HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
   HybridWs w{};
   const size_t nblk = static_cast<size_t>((d->T + 255) / 256);
+  const size_t cap = static_cast<size_t>(max_dense_rows);
+  const int sp = dense_splits(d);
   w.block_dense = 0;
   w.h = align256(nblk * 4);
-  w.total = w.h + align256(static_cast<size_t>(max_dense_rows) * d->d_ff * elem_bytes(d));
+  w.part = w.h + align256(cap * d->d_ff * elem_bytes(d));
+  w.total = w.part + (sp > 1 ? align256(static_cast<size_t>(sp) * cap * d->d_model * 4) : 0);
   return w;
 }
 
 // Workspace layout of the backward.
 struct BwdWs {
-  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, total;
+  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, dx_part, total;
 };
 BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   BwdWs w{};
@@ -80,6 +89,8 @@ BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   w.dg_d = o;       o += align256(cap * F * eb);
   w.du_d = o;       o += align256(cap * F * eb);
   w.h_d = o;        o += align256(cap * F * eb);
+  const int sp = dense_splits(d);
+  w.dx_part = o;    o += sp > 1 ? align256(static_cast<size_t>(sp) * cap * static_cast<size_t>(d->d_model) * 4) : 0;
   w.total = o;
   return w;
 }
@@ -239,6 +250,8 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
   dn.M = route->max_dense_rows;
   dn.d = d->d_model;
   dn.F = d->d_ff;
+  dn.splits = dense_splits(d);
+  dn.part = reinterpret_cast<float*>(wsb + hw.part);
   return from_hip(twell::launch_down(dn, d->dtype, s));
 }
 
@@ -298,6 +311,8 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.dg_d = wsb + bw.dg_d;
   a.du_d = wsb + bw.du_d;
   a.h_d = wsb + bw.h_d;
+  a.dx_splits = dense_splits(d);
+  a.dx_part = reinterpret_cast<float*>(wsb + bw.dx_part);
   TWELL_TRY(from_hip(twell::launch_bwd_sparse(a, d->dtype, s)));
   return from_hip(twell::launch_bwd_dense(a, d->dtype, s));
 }
