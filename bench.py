@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=20,
                     help="iterations of the cold-cache timing (a 1 GiB write before each; 0 = skip)")
     ap.add_argument("--no-hipblaslt", action="store_true", help="skip the torch.matmul dense sanity point")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step line: the density sweep of the 2B-class shape (0.1..5%% and a "
+                         "16-token batch), TwELL (plain and hybrid) against the dense FFN; prints one JSON line")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, run one plain fp32 negation of this many MiB (reads and writes "
                          "exactly that much): the reference dispatch that scales rocprofv3 FETCH_SIZE / "
@@ -207,6 +210,71 @@ def hipblaslt_dense(x, wg, wu, wd, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def density_sweep(T, W, args):
+    """TwELL forward (pack + fused, and pack + hybrid) against the library's
+    dense FFN over the sweep densities at the 2B-class shape, plus a 16-token
+    batch at 0.5%: per point the measured density, overflowing tiles, dense
+    rows of the hybrid route, times, speed-ups and the fused kernel's gathered
+    rate."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    points = [(rho, None) for rho in W.SWEEP_RHOS] + [(0.005, 16)]
+    out = []
+    for rho, t_over in points:
+        w = W.workload(5, rho=rho, T=t_over)
+        inp = W.make_inputs(w)
+
+        def dev(raw):
+            return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+
+        x, wg, wu, wd = (dev(inp[k + "_raw"]) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
+        desc = T.Desc(w.T, w.d_model, w.d_ff, w.tile_n, w.slots, w.dtype)
+        cap = min(w.T, args.max_dense_rows)
+        act = T.alloc_act(desc)
+        route = T.alloc_route(desc, cap)
+        sz = T.sizes(desc, cap)
+        wsh = torch.empty(sz["ws_hybrid"], dtype=torch.uint8, device="cuda")
+        wsd = torch.empty(sz["ws_dense_fwd"], dtype=torch.uint8, device="cuda")
+        y = torch.empty((w.T, w.d_model), dtype=torch.bfloat16, device="cuda")
+        stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+        T.twell_pack(desc, x, wg, act, stats=stats, stream=stream)
+        T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, wsh, stream=stream)
+        torch.cuda.synchronize()
+        nnz, ovf = int(stats[1]), int(stats[0])
+        n_rows = route.n_rows.cpu().tolist()
+
+        def timed(fn, k=args.steps, warm=args.warmup):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(k):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+
+        pack_ms = timed(lambda: T.twell_pack(desc, x, wg, act, stream=stream))
+        fused_ms = timed(lambda: T.twell_ffn_fwd(desc, x, act, wu, wd, y, stream=stream))
+        hyb_ms = timed(lambda: T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, wsh, stream=stream))
+        dense_ms = timed(lambda: T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, y, wsd, stream=stream))
+        gathered = nnz * 2 * w.d_model * 2
+        out.append({"rho_target": rho, "T": w.T, "measured_density": round(nnz / (w.T * w.d_ff), 6),
+                    "overflow_tiles": ovf, "dense_rows": n_rows[1], "dense_over_cap": n_rows[2],
+                    "pack_ms": round(pack_ms, 4), "fused_ms": round(fused_ms, 4),
+                    "hybrid_fwd_ms": round(hyb_ms, 4), "dense_ms": round(dense_ms, 4),
+                    "speedup_plain": round(dense_ms / (pack_ms + fused_ms), 3),
+                    "speedup_hybrid": round(dense_ms / (pack_ms + hyb_ms), 3),
+                    "fused_gathered_gbs": round(gathered / (fused_ms * 1e-3) / 1e9, 1),
+                    "gate_pack_tflops": round(2.0 * w.T * w.d_model * w.d_ff / (pack_ms * 1e-3) / 1e12, 1)})
+        print(json.dumps({"sweep_point": out[-1]}), file=sys.stderr, flush=True)
+        del x, wg, wu, wd, act, route, wsh, wsd, y
+        torch.cuda.empty_cache()
+    return out
+
+
 def train_step(T, W, args, steps, warmup):
     """Time one training step of the FFN layer on the training workload:
     twell_pack + twell_ffn_fwd_hybrid + twell_ffn_bwd (HIP events per phase)."""
@@ -273,6 +341,10 @@ def main():
     from activation_sparse_feedforward_amd import workloads as W
 
     T.library()  # fail loudly if the HIP library is missing
+    if args.sweep:
+        print(json.dumps({"sweep": "llama2B_ffn_sweep_T16384_d2048_F8192", "steps": args.steps,
+                          "warmup": args.warmup, "points": density_sweep(T, W, args)}), flush=True)
+        return
     w = W.workload(args.config, T=args.T, rho=args.rho)
     inp = W.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
