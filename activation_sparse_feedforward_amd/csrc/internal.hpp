@@ -33,6 +33,18 @@ struct FusedArgs {
   int32_t d, F, tile_n, C;
 };
 
+// Classic ELL construction (baseline): dense ReLU(g) [T x F] written to `dense`,
+// then converted to the TwELL planes by a second kernel.
+struct ClassicArgs {
+  const void* x;         // [T x d]
+  const void* w_gate_t;  // [F x d]
+  void* dense;           // [T x F] dtype (workspace)
+  int64_t T;
+  int32_t d, F, tile_n, C;
+  int32_t* count;
+  uint8_t* idx;
+  void* val;
+};
 // Hybrid router: flags[t] (1 = dense), ascending ell_rows / dense_rows lists,
 // n_rows = {n_ell, n_dense, n_dense_over_cap}.
 struct RouteArgs {
@@ -127,6 +139,7 @@ hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
 // gateup256 (all M rows), down256.  dn.h must be g.h.
 hipError_t launch_dense256(const GateUpArgs& g, const DownArgs& dn, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_classic_pack(const ClassicArgs& a, int dtype, hipStream_t s);
 // out[row(m), :] = round(sum_{s < splits} part[s][m][:]) for m < n_rows (n_rows =
 // *n_rows_dev, row(m) = rows[m] or m), summed in ascending s.  d % 4 == 0.
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, const int32_t* n_rows_dev,

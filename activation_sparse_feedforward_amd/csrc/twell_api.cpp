@@ -123,6 +123,7 @@ twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_size
   const HybridWs hw = hybrid_ws(d, max_dense_rows);
   out->ws_hybrid = hw.total;
   out->ws_bwd = bwd_ws(d, max_dense_rows).total;
+  out->ws_pack_classic = T * static_cast<size_t>(d->d_ff) * eb;
   return TWELL_OK;
 }
 
@@ -316,6 +317,32 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.dx_part = reinterpret_cast<float*>(wsb + bw.dx_part);
   TWELL_TRY(from_hip(twell::launch_bwd_sparse(a, d->dtype, s)));
   return from_hip(twell::launch_bwd_dense(a, d->dtype, s));
+}
+
+twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                                void* ws, size_t ws_bytes, void* stream) {
+  TWELL_TRY(check_desc(d));
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_act(act));
+  TWELL_TRY(check_dense_ptr(ws));
+  twell_sizes_t sz;
+  TWELL_TRY(twell_sizes(d, 0, &sz));
+  if (ws_bytes < sz.ws_pack_classic) return TWELL_EINVAL;
+  twell::ClassicArgs a{};
+  a.x = x;
+  a.w_gate_t = w_gate_t;
+  a.dense = ws;
+  a.T = d->T;
+  a.d = d->d_model;
+  a.F = d->d_ff;
+  a.tile_n = d->tile_n;
+  a.C = d->slots;
+  a.count = act.count;
+  a.idx = act.idx;
+  a.val = act.val;
+  return from_hip(twell::launch_classic_pack(a, d->dtype, static_cast<hipStream_t>(stream)));
 }
 
 twell_status twell_dense_ffn_fwd(const twell_desc* d, const void* x, const void* w_gate_t,

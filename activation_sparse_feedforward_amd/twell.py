@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libtwell.so")
 TWELL_OK, TWELL_EINVAL, TWELL_EUNSUPPORTED, TWELL_EHIP = 0, 1, 2, 3
 TWELL_FP32, TWELL_BF16 = 0, 1
 
-EXPORTED = ("twell_sizes", "twell_pack", "twell_ffn_fwd", "twell_ffn_fwd_hybrid", "twell_ffn_bwd",
-            "twell_dense_ffn_fwd", "twell_status_str")
+EXPORTED = ("twell_sizes", "twell_pack", "twell_pack_classic", "twell_ffn_fwd", "twell_ffn_fwd_hybrid",
+            "twell_ffn_bwd", "twell_dense_ffn_fwd", "twell_status_str")
 
 
 class TwellError(RuntimeError):
@@ -48,7 +48,8 @@ class CRoute(ctypes.Structure):
 
 class CSizes(ctypes.Structure):
     _fields_ = [("count", ctypes.c_size_t), ("idx", ctypes.c_size_t), ("val", ctypes.c_size_t),
-                ("ws_dense_fwd", ctypes.c_size_t), ("ws_hybrid", ctypes.c_size_t), ("ws_bwd", ctypes.c_size_t)]
+                ("ws_dense_fwd", ctypes.c_size_t), ("ws_hybrid", ctypes.c_size_t), ("ws_bwd", ctypes.c_size_t),
+                ("ws_pack_classic", ctypes.c_size_t)]
 
 
 _lib = None
@@ -70,6 +71,7 @@ def library() -> ctypes.CDLL:
             "twell_ffn_fwd_hybrid": (ST, [D, P, P, CAct, P, P, P, R, P, SZ, P]),
             "twell_ffn_bwd": (ST, [D, P, CAct, R, P, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]),
             "twell_pack": (ST, [D, P, P, CAct, P, P, P]),
+            "twell_pack_classic": (ST, [D, P, P, CAct, P, SZ, P]),
             "twell_ffn_fwd": (ST, [D, P, CAct, P, P, P, P]),
             "twell_dense_ffn_fwd": (ST, [D, P, P, P, P, P, P, SZ, P]),
             "twell_status_str": (ctypes.c_char_p, [ST]),
@@ -204,6 +206,18 @@ def twell_pack(desc: Desc, x, w_gate_t, act: Act, stats=None, gate_dbg=None, str
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
         _ptr(stats, "stats", 16, torch.int64), _ptr(gate_dbg, "gate_dbg", desc.T * desc.d_ff * e, dt),
         _stream(stream)))
+
+
+def twell_pack_classic(desc: Desc, x, w_gate_t, act: Act, ws, stream=None):
+    """Baseline: dense gate GEMM writing ReLU(g) to ws, then a conversion kernel
+    to the same TwELL planes (see include/twell.h)."""
+    e = 2 if desc.dtype == "bf16" else 4
+    dt = desc.torch_dtype
+    need = sizes(desc)["ws_pack_classic"]
+    _check("twell_pack_classic", library().twell_pack_classic(
+        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act), _ptr(ws, "ws", need),
+        ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
 
 
 def twell_ffn_fwd(desc: Desc, x, act: Act, w_up_t, w_down, y, stream=None):

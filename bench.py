@@ -37,9 +37,12 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload id (default: the 2B-class inference shape)")
     ap.add_argument("--rho", type=float, default=None, help="override the gate density (sweep workload)")
     ap.add_argument("--T", type=int, default=None, help="override the token count")
+    ap.add_argument("--d-ff", type=int, default=None,
+                    help="override d_ff (e.g. 1024: one GPU's share of the 2B-class FFN split 8 ways over neurons)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    ap.add_argument("--no-classic", action="store_true", help="skip the classic two-kernel ELL baseline")
     ap.add_argument("--no-train", action="store_true", help="skip the training-step measurement")
     ap.add_argument("--train-config", type=int, default=4, help="workload of the training-step measurement")
     ap.add_argument("--max-dense-rows", type=int, default=1024)
@@ -345,7 +348,9 @@ def main():
         print(json.dumps({"sweep": "llama2B_ffn_sweep_T16384_d2048_F8192", "steps": args.steps,
                           "warmup": args.warmup, "points": density_sweep(T, W, args)}), flush=True)
         return
-    w = W.workload(args.config, T=args.T, rho=args.rho)
+    w = W.workload(args.config, T=args.T, rho=args.rho, d_ff=args.d_ff)
+    overridden = args.T is not None or args.rho is not None or args.d_ff is not None
+    wname = w.name if not overridden else f"{w.name}@T{w.T}_F{w.d_ff}_rho{w.rho}"
     inp = W.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
@@ -430,6 +435,31 @@ def main():
             dense["torch_matmul_sanity"] = {"ms_per_step": round(hb, 4), "tflops": round(flops / hb / 1e9, 1)}
             torch.cuda.empty_cache()
 
+    # classic ELL construction (dense gate write-back + conversion kernel), same fused kernel after it
+    classic = None
+    if not args.no_classic:
+        wsc = torch.empty(T.sizes(desc)["ws_pack_classic"], dtype=torch.uint8, device="cuda")
+        act_c = T.alloc_act(desc)
+        for _ in range(args.warmup):
+            T.twell_pack_classic(desc, x, wg, act_c, wsc, stream=stream)
+        torch.cuda.synchronize()
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for k in range(K):
+            evc[k][0].record(stream)
+            T.twell_pack_classic(desc, x, wg, act_c, wsc, stream=stream)
+            evc[k][1].record(stream)
+            T.twell_ffn_fwd(desc, x, act_c, wu, wd, y, stream=stream)
+            evc[k][2].record(stream)
+        torch.cuda.synchronize()
+        cpk = float(np.mean([e[0].elapsed_time(e[1]) for e in evc]))
+        cfu = float(np.mean([e[1].elapsed_time(e[2]) for e in evc]))
+        classic = {"pack_classic_ms": round(cpk, 4), "fused_ms": round(cfu, 4), "ms_per_step": round(cpk + cfu, 4),
+                   "dense_relu_bytes_written_and_read": 2 * w.T * w.d_ff * (2 if w.dtype == "bf16" else 4),
+                   "epilogue_pack_speedup": round(cpk / pack_ms, 3),
+                   "step_speedup_of_epilogue_packing": round((cpk + cfu) / (pack_ms + fused_ms), 3)}
+        del wsc, act_c
+        torch.cuda.empty_cache()
+
     cold = None
     if args.cold_iters > 0:
         cold = cold_timing([("gate_pack", lambda: T.twell_pack(desc, x, wg, act, stream=stream)),
@@ -450,12 +480,12 @@ def main():
         ach = gate_flop / (pack_ms * 1e-3) / 1e12
         roof = {"kernel": "gate_pack", "bound": "mfma", "achieved": round(ach, 1), "peak": peak_mm,
                 "unit": "TFLOP/s", "frac": round(ach / peak_mm, 4),
-                "traffic": measured_traffic("gate_pack", src["gate_pack"], 1)}
+                "traffic": None if overridden or args.config != 3 else measured_traffic("gate_pack", src["gate_pack"], 1)}
     else:
         ach = fused_bytes / (fused_ms * 1e-3) / 1e9
         roof = {"kernel": "fused_updown", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic("fused_updown", src["fused_updown"], 1)}
+                "traffic": None if overridden or args.config != 3 else measured_traffic("fused_updown", src["fused_updown"], 1)}
 
     out = {
         "metric": "TwELL FFN tokens/sec at 99.5% act. sparsity; speedup vs dense; % roofline",
@@ -470,7 +500,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded PCG64; gate density set by a column-0 offset)",
-        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "d_ff": w.d_ff, "tile_n": w.tile_n,
+        "config": {"workload": wname, "T": w.T, "d_model": w.d_model, "d_ff": w.d_ff, "tile_n": w.tile_n,
                    "slots": w.slots, "target_density": w.rho if w.density == "uniform" else w.density},
         "roofline": roof,
         "measured_density": round(density, 6),
@@ -481,6 +511,7 @@ def main():
                          "gathered_gbs": round(gathered_bytes / (fused_ms * 1e-3) / 1e9, 1),
                          "gathered_bytes": int(gathered_bytes), "required_bytes": int(fused_bytes)},
         "dense_ffn": dense,
+        "classic_ell": classic,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 3) if dense else None,
         "cold_ms": cold,
         "speedup_vs_dense_cold": (round(dense["cold_ms"]["median"] / cold["total"]["median"], 3)

@@ -101,6 +101,7 @@ typedef struct {
   size_t ws_dense_fwd; /* twell_dense_ffn_fwd: h [T x d_ff] + W_down^T         */
   size_t ws_hybrid;    /* workspace of twell_ffn_fwd_hybrid (max_dense_rows)  */
   size_t ws_bwd;       /* workspace of twell_ffn_bwd (max_dense_rows)         */
+  size_t ws_pack_classic; /* twell_pack_classic: dense ReLU(g) [T x d_ff]      */
 } twell_sizes_t;
 
 /* Fill *out for descriptor *d and a dense-row capacity (>= 0).  Host only.
@@ -120,6 +121,18 @@ twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_size
  *        write-back the method exists to avoid, so leave it NULL when timing). */
 twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
                         int64_t* stats, void* gate_dbg, void* stream);
+
+/* The same TwELL planes built the classic way, as a baseline for twell_pack:
+ * [P2 §Problema and §TwELL-vs-ELL: converting a dense activation tensor to a
+ * sparse format in a separate kernel costs an extra launch and a full write
+ * and read of that tensor, which eats the saving.]
+ * Kernel 1: the gate GEMM (same accumulation order as twell_pack) writes
+ *           ReLU(g) rounded to dtype densely into ws, [T x d_ff];
+ * Kernel 2: one wave per (row, tile) converts it to TwELL.
+ * act is written exactly as twell_pack writes it (byte-identical planes).
+ * ws: twell_sizes().ws_pack_classic bytes. */
+twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Fused up + down projection on TwELL input, in ONE kernel dispatch.
  * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down

@@ -54,6 +54,7 @@ def test_sizes_values():
     assert s["idx"] == 16384 * 64 * 16
     assert s["val"] == 16384 * 64 * 16 * 2
     assert s["ws_dense_fwd"] == 16384 * 8192 * 2 + 2048 * 8192 * 2  # h, then W_down^T
+    assert s["ws_pack_classic"] == 16384 * 8192 * 2                    # dense ReLU(g)
     h = T.sizes(T.Desc(16384, 2048, 8192, 128, 16, "bf16"), max_dense_rows=1000)
     assert h["ws_hybrid"] >= 1000 * 8192 * 2 + 64 * 4
     d = T.Desc(16, 512, 1024, 128, 16, "bf16").c()
@@ -73,6 +74,9 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.twell_dense_ffn_fwd(ctypes.byref(d), P, P, P, P, P, P, 100, None) == T.TWELL_EINVAL  # ws too small
     assert lib.twell_dense_ffn_fwd(ctypes.byref(d), P, P, P, P, P, None, 1 << 30, None) == T.TWELL_EINVAL
     assert lib.twell_pack(None, P, P, act, None, None, None) == T.TWELL_EINVAL
+    assert lib.twell_pack_classic(ctypes.byref(d), P, P, act, P, 100, None) == T.TWELL_EINVAL  # ws too small
+    assert lib.twell_pack_classic(ctypes.byref(d), P, P, act, None, 1 << 30, None) == T.TWELL_EINVAL
+    assert lib.twell_pack_classic(ctypes.byref(d), P, P + 2, act, P, 1 << 30, None) == T.TWELL_EINVAL
     r = T.CRoute(P, P, P, P, 10)
     assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, None, P, 1 << 30, None) == T.TWELL_EINVAL
     assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, ctypes.byref(r), P, 16, None) == T.TWELL_EINVAL
@@ -87,6 +91,7 @@ def test_empty_batch_is_a_noop():
     assert lib.twell_pack(ctypes.byref(d), None, None, T.CAct(0, 0, 0), None, None, None) == T.TWELL_OK
     assert lib.twell_ffn_fwd(ctypes.byref(d), None, T.CAct(0, 0, 0), None, None, None, None) == T.TWELL_OK
     assert lib.twell_dense_ffn_fwd(ctypes.byref(d), None, None, None, None, None, None, 0, None) == T.TWELL_OK
+    assert lib.twell_pack_classic(ctypes.byref(d), None, None, T.CAct(0, 0, 0), None, 0, None) == T.TWELL_OK
 
 
 def test_status_strings():

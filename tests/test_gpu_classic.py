@@ -1,0 +1,58 @@
+"""GPU parity of the classic ELL baseline (twell_pack_classic: dense gate GEMM
+writing ReLU(g), then a conversion kernel) through the C ABI.
+
+twell_pack is pinned bit-exactly to the oracle packer elsewhere; the classic
+path must produce byte-identical TwELL planes, and its dense ReLU(g) must equal
+the pack kernel's own dense debug output (same accumulation order)."""
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_feedforward_amd import twell as T
+from activation_sparse_feedforward_amd import workloads as W
+from oracle import twell_oracle as O
+from _helpers import desc_for, dev, host64, poison_, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("c1 fp32 T_n=64", W.workload(1)),
+    ("c2 ragged T", W.workload(2, T=1000)),
+    ("c3 shape T=300", W.workload(3, T=300)),
+    ("rho 5% (overflow)", W.workload(5, T=300, rho=0.05)),
+    ("C = T_n", W.workload(2, T=260, rho=0.3)),
+    ("T=1", W.workload(2, T=1)),
+    ("c3 full", W.workload(3)),
+]
+
+
+@pytest.mark.parametrize("label,w", CASES, ids=[c[0] for c in CASES])
+def test_classic_equals_epilogue_pack(label, w):
+    if label == "C = T_n":
+        import dataclasses
+        w = dataclasses.replace(w, slots=w.tile_n)
+    say(f"[gpu case] classic {label} T={w.T} F={w.d_ff} C={w.slots} {w.dtype}")
+    inp = W.make_inputs(w)
+    desc = desc_for(w)
+    x = dev(inp["x_raw"], w.dtype)
+    wg = dev(inp["w_gate_t_raw"], w.dtype)
+    a1, a2 = T.alloc_act(desc), T.alloc_act(desc)
+    for t in list(a1) + list(a2):
+        poison_(t)
+    gate = poison_(torch.empty((desc.T, desc.d_ff), dtype=desc.torch_dtype, device="cuda"))
+    T.twell_pack(desc, x, wg, a1, gate_dbg=gate)
+    ws = poison_(torch.empty(T.sizes(desc)["ws_pack_classic"], dtype=torch.uint8, device="cuda"))
+    T.twell_pack_classic(desc, x, wg, a2, ws)
+    torch.cuda.synchronize()
+    dense = ws[: desc.T * desc.d_ff * (2 if w.dtype == "bf16" else 4)].view(desc.torch_dtype).view(desc.T, desc.d_ff)
+    assert torch.equal(dense.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                       gate.view(torch.int16 if w.dtype == "bf16" else torch.int32))
+    for p1, p2, name in zip(a1, a2, ("count", "idx", "val")):
+        b1 = p1.view(torch.uint8) if p1.dtype != torch.uint8 else p1
+        b2 = p2.view(torch.uint8) if p2.dtype != torch.uint8 else p2
+        assert torch.equal(b1, b2), name
+    if desc.T <= 1000:  # and against the oracle packer on the dense output
+        cnt, idx, val = O.twell_pack(host64(gate), desc.tile_n, desc.slots)
+        assert np.array_equal(a2.count.cpu().numpy(), cnt)
+        assert np.array_equal(a2.idx.cpu().numpy(), idx)
+        assert np.array_equal(host64(a2.val), val)
