@@ -31,6 +31,12 @@ struct FusedArgs {
   const int32_t* n_rows_dev;  // device count of `rows` or null
   int64_t T;                  // rows of x / y; also the upper bound of the row list
   int32_t d, F, tile_n, C;
+  // split mode (launch_fused_split): every row of the list is cut into
+  // `groups` tile ranges, one wave each, whose fp32 partial outputs go to
+  // part[group][i_row][d] (i_row < part_rows); y is then not written.
+  int32_t groups;
+  float* part;
+  int64_t part_rows;
 };
 
 // Classic ELL construction (baseline): dense ReLU(g) [T x F] written to `dense`,
@@ -57,6 +63,13 @@ struct RouteArgs {
   int32_t* ell_rows;     // [T]
   int32_t* dense_rows;   // [cap]
   int32_t* n_rows;       // [3]
+  // light / heavy split of the ELL rows (launch_route_split; null = not used)
+  int32_t* row_total;    // [T] non-zeros of each row (sum of its counts)
+  int32_t* block_total;  // [ceil(T/256)] sum of row_total per block
+  int32_t* light_rows;   // [T]
+  int32_t* heavy_rows;   // [heavy_cap]
+  int32_t* split_n;      // [2] {n_light, n_heavy (may exceed heavy_cap: clamp)}
+  int64_t heavy_cap;
 };
 
 // h[m, j] = ReLU(x[row(m)] . w_gate_t[j]) * (x[row(m)] . w_up_t[j]) for m < n_rows,
@@ -133,12 +146,16 @@ struct BwdArgs {
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
 hipError_t launch_gate_pack(const PackArgs& a, int dtype, hipStream_t s);
 hipError_t launch_fused_updown(const FusedArgs& a, int dtype, hipStream_t s);
+hipError_t launch_fused_split(const FusedArgs& a, int dtype, hipStream_t s);
 hipError_t launch_gateup(const GateUpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_down(const DownArgs& a, int dtype, hipStream_t s);
 // Full dense FFN on the 256 x 256 core: transpose w_down into dn.w_down_t,
 // gateup256 (all M rows), down256.  dn.h must be g.h.
 hipError_t launch_dense256(const GateUpArgs& g, const DownArgs& dn, int dtype, hipStream_t s);
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// After launch_route: split the ELL rows into light rows and at most heavy_cap
+// heavy rows (row total > max(2 C, 2 x the mean row total)).
+hipError_t launch_route_split(const RouteArgs& a, hipStream_t s);
 hipError_t launch_classic_pack(const ClassicArgs& a, int dtype, hipStream_t s);
 // out[row(m), :] = round(sum_{s < splits} part[s][m][:]) for m < n_rows (n_rows =
 // *n_rows_dev, row(m) = rows[m] or m), summed in ascending s.  d % 4 == 0.

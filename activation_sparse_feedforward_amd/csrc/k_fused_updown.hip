@@ -115,20 +115,36 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }  // namespace
 
 // NV = 16-byte vectors per lane per row: d_model = NV * 64 * Vec<E>::N.
-template <class E, int NV>
+// SPLIT: each row of the list is cut into p.groups tile ranges, one wave per
+// (row, range), writing its fp32 partial y to p.part[range][i_row][:] for a
+// fixed-order reduction afterwards (used for the few rows with far more
+// non-zeros than the rest, which would otherwise serialise on one wave).
+template <class E, int NV, bool SPLIT>
 __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel(FusedArgs p) {
   constexpr int kN = Vec<E>::N;
   constexpr int kU = neurons_in_flight<NV>();
   __shared__ int2 list_all[kWavesPerBlock][kListCap];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
-  const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
-  if (i_row >= n_rows) return;  // whole wave exits together; no block barrier below
-  const int64_t t = p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row;
-  int2* list = list_all[wave];
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave;
+  int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
   const int d = p.d, C = p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
+  int64_t i_row = unit;
+  int grp = 0, b_begin = 0, b_end = n_t;
+  if constexpr (SPLIT) {
+    n_rows = min(n_rows, p.part_rows);
+    if (unit >= n_rows * p.groups) return;
+    i_row = unit / p.groups;
+    grp = static_cast<int>(unit - i_row * p.groups);
+    const int tg = (n_t + p.groups - 1) / p.groups;
+    b_begin = min(n_t, grp * tg);
+    b_end = min(n_t, b_begin + tg);
+  } else {
+    if (i_row >= n_rows) return;  // whole wave exits together; no block barrier below
+  }
+  const int64_t t = p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row;
+  int2* list = list_all[wave];
 
   // x[t] (kept in storage form) and the fp32 y accumulator, lane-strided 16-byte chunks
   u32x4_t xs[NV];
@@ -144,13 +160,13 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
   }
 
   const int chunk_tiles = min(kWave, kListCap / C);
-  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+  for (int b0 = b_begin; b0 < b_end; b0 += chunk_tiles) {
     // ---- build the (j, a) list of this chunk of tiles, ascending j
     const int b = b0 + lane;
     int cnt = 0;
     // counts are clamped to [0, C] and tile-local indices masked to the tile
     // width (a power of two), so even a corrupted TwELL stays in bounds
-    if (lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
+    if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
     const int incl = wave_incl_scan(cnt, lane);
     const int total = __shfl(incl, 63);
     const int off = incl - cnt;
@@ -214,9 +230,19 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
     __builtin_amdgcn_wave_barrier();
   }
 
-  u32x4_t* yr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.y) + t * d * E::kBytes);
+  if constexpr (SPLIT) {
+    float* o = p.part + (static_cast<int64_t>(grp) * p.part_rows + i_row) * d;
 #pragma unroll
-  for (int v = 0; v < NV; ++v) yr[v * kWave + lane] = Vec<E>::pack(yf[v]);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < kN; i += 4)
+        *reinterpret_cast<float4*>(o + (v * kWave + lane) * kN + i) =
+            make_float4(yf[v][i], yf[v][i + 1], yf[v][i + 2], yf[v][i + 3]);
+  } else {
+    u32x4_t* yr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.y) + t * d * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) yr[v * kWave + lane] = Vec<E>::pack(yf[v]);
+  }
 }
 
 // Lockstep variant (d_model up to 2048 in bf16): a workgroup of 16 waves, each
@@ -391,8 +417,38 @@ static hipError_t launch_sync_t(const FusedArgs& a, hipStream_t s) {
 template <class E, int NV>
 static hipError_t launch_fused_t(const FusedArgs& a, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((a.T + kWavesPerBlock - 1) / kWavesPerBlock));
-  hipLaunchKernelGGL((fused_updown_kernel<E, NV>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+  hipLaunchKernelGGL((fused_updown_kernel<E, NV, false>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
   return hipGetLastError();
+}
+
+template <class E, int NV>
+static hipError_t launch_split_t(const FusedArgs& a, hipStream_t s) {
+  const int64_t units = a.part_rows * a.groups;
+  dim3 grid(static_cast<unsigned>((units + kWavesPerBlock - 1) / kWavesPerBlock));
+  hipLaunchKernelGGL((fused_updown_kernel<E, NV, true>), grid, dim3(kWavesPerBlock * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_split_e(const FusedArgs& a, hipStream_t s) {
+  if (a.part_rows <= 0 || a.groups <= 0) return hipSuccess;
+  switch (a.d / (kWave * Vec<E>::N)) {
+    case 1: return launch_split_t<E, 1>(a, s);
+    case 2: return launch_split_t<E, 2>(a, s);
+    case 3: return launch_split_t<E, 3>(a, s);
+    case 4: return launch_split_t<E, 4>(a, s);
+    case 5: return launch_split_t<E, 5>(a, s);
+    case 6: return launch_split_t<E, 6>(a, s);
+    case 7: return launch_split_t<E, 7>(a, s);
+    case 8: return launch_split_t<E, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fused_split(const FusedArgs& a, int dtype, hipStream_t s) {
+  hipError_t e = dtype == 1 ? launch_split_e<EBf16>(a, s) : launch_split_e<EF32>(a, s);
+  if (e != hipSuccess || a.part_rows <= 0 || a.groups <= 0) return e;
+  return launch_splitk_reduce(a.part, a.groups, a.part_rows, a.n_rows_dev, a.rows, a.y, a.d, dtype, s);
 }
 
 template <class E>

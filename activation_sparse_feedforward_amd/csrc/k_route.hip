@@ -26,23 +26,39 @@ constexpr int kRouteBlock = 256;
 __global__ __launch_bounds__(kRouteBlock) void route_flags_kernel(RouteArgs p) {
   __shared__ int wsum[kRouteBlock / kWave];
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
-  int dense = 0;
+  __shared__ int wtot[kRouteBlock / kWave];
+  int dense = 0, total = 0;
   if (t < p.T) {
     const int32_t* c = p.count + t * p.n_t;
     int mx = 0;
-    for (int b = 0; b < p.n_t; ++b) mx = max(mx, c[b]);
+    for (int b = 0; b < p.n_t; ++b) {
+      const int v = c[b];
+      mx = max(mx, v);
+      total += max(v, 0);
+    }
     dense = mx > p.C ? 1 : 0;
     p.flags[t] = static_cast<uint8_t>(dense);
+    if (p.row_total) p.row_total[t] = total;
   }
-  int s = dense;
+  int s = dense, st = total;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+  for (int o = 32; o >= 1; o >>= 1) {
+    s += __shfl_xor(s, o);
+    st += __shfl_xor(st, o);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wsum[threadIdx.x >> 6] = s;
+    wtot[threadIdx.x >> 6] = st;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int w = 0; w < kRouteBlock / kWave; ++w) tot += wsum[w];
+    int tot = 0, tt = 0;
+    for (int w = 0; w < kRouteBlock / kWave; ++w) {
+      tot += wsum[w];
+      tt += wtot[w];
+    }
     p.block_dense[blockIdx.x] = tot;
+    if (p.block_total) p.block_total[blockIdx.x] = tt;
   }
 }
 
@@ -89,12 +105,68 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(RouteArgs p)
     }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (p.split_n) {  // launch_route_split appends to these after this kernel
+      p.split_n[0] = 0;
+      p.split_n[1] = 0;
+    }
     const int64_t total = sum_upto;
     const int64_t kept = total < p.cap ? total : p.cap;
     p.n_rows[0] = static_cast<int32_t>(p.T - kept);
     p.n_rows[1] = static_cast<int32_t>(kept);
     p.n_rows[2] = static_cast<int32_t>(total - kept);
   }
+}
+
+// One thread per ELL-list position.  Heavy rows (many more non-zeros than the
+// batch's mean row) would hold a lockstep workgroup of the fused kernel back
+// at every chunk barrier; they are listed apart (up to heavy_cap; any excess
+// stays light) and cut into tile ranges by launch_fused_split.  Appends use
+// one atomic per wave and category, so the lists are in no particular order
+// (every row's own arithmetic does not depend on it).
+__global__ __launch_bounds__(kRouteBlock) void route_split_kernel(RouteArgs p) {
+  __shared__ float s_mean;
+  const int nblk = static_cast<int>((p.T + kRouteBlock - 1) / kRouteBlock);
+  if (threadIdx.x == 0) {
+    long long tot = 0;
+    for (int b = 0; b < nblk; ++b) tot += p.block_total[b];
+    s_mean = p.T > 0 ? static_cast<float>(static_cast<double>(tot) / static_cast<double>(p.T)) : 0.f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  const int64_t n_ell = p.n_rows[0];
+  const bool live = i < n_ell;
+  int32_t t = 0;
+  bool heavy = false;
+  if (live) {
+    t = p.ell_rows[i];
+    const float thr = fmaxf(2.f * p.C, 2.f * s_mean);
+    heavy = static_cast<float>(p.row_total[t]) > thr;
+  }
+  // heavy appends first; slots past the cap fall back to the light list
+  const uint64_t mh = __builtin_amdgcn_ballot_w64(live && heavy);
+  int hbase = 0;
+  if (lane == 0 && mh) hbase = atomicAdd(p.split_n + 1, static_cast<int>(__popcll(mh)));
+  hbase = __shfl(hbase, 0);
+  const int hslot = hbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mh >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mh), 0u)));
+  const bool to_heavy = live && heavy && hslot < p.heavy_cap;
+  if (to_heavy) p.heavy_rows[hslot] = t;
+  const bool to_light = live && !to_heavy;
+  const uint64_t ml = __builtin_amdgcn_ballot_w64(to_light);
+  int lbase = 0;
+  if (lane == 0 && ml) lbase = atomicAdd(p.split_n + 0, static_cast<int>(__popcll(ml)));
+  lbase = __shfl(lbase, 0);
+  const int lslot = lbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ml >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ml), 0u)));
+  if (to_light) p.light_rows[lslot] = t;
+}
+
+hipError_t launch_route_split(const RouteArgs& a, hipStream_t s) {
+  const unsigned nblk = static_cast<unsigned>((a.T + kRouteBlock - 1) / kRouteBlock);
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_split_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {

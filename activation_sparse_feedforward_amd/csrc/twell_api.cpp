@@ -53,21 +53,41 @@ size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 // Split-K factor of the dense rows' GEMMs that reduce over d_ff.
 int dense_splits(const twell_desc* d) { return twell::split_k_for(d->d_ff, 128 / elem_bytes(d)); }
 
+// Heavy ELL rows of the hybrid forward (row total > max(2 C, 2 x mean)): at
+// most kHeavyCap of them are cut into heavy_groups() tile ranges each.
+constexpr int64_t kHeavyCap = 1024;
+int64_t heavy_cap(const twell_desc* d) { return d->T < kHeavyCap ? d->T : kHeavyCap; }
+int heavy_groups(const twell_desc* d) {
+  const int n_t = d->d_ff / d->tile_n;
+  return n_t < 8 ? n_t : 8;
+}
+
 // Workspace layout of the hybrid forward: router block counts, the dense rows'
-// hidden activations h [max_dense_rows x d_ff], and the split-K partials of
-// their down GEMM [splits x max_dense_rows x d_model] fp32 (splits > 1 only).
+// hidden activations h [max_dense_rows x d_ff], the split-K partials of their
+// down GEMM [splits x max_dense_rows x d_model] fp32 (splits > 1 only), then
+// the light / heavy split of the ELL rows (row totals, block totals, the two
+// lists, their counters) and the heavy rows' partial outputs
+// [groups x heavy_cap x d_model] fp32.
 struct HybridWs {
-  size_t block_dense, h, part, total;
+  size_t block_dense, h, part, row_total, block_total, light, heavy, split_n, heavy_part, total;
 };
 HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
   HybridWs w{};
-  const size_t nblk = static_cast<size_t>((d->T + 255) / 256);
+  const size_t T = static_cast<size_t>(d->T);
+  const size_t nblk = (T + 255) / 256;
   const size_t cap = static_cast<size_t>(max_dense_rows);
   const int sp = dense_splits(d);
   w.block_dense = 0;
   w.h = align256(nblk * 4);
   w.part = w.h + align256(cap * d->d_ff * elem_bytes(d));
-  w.total = w.part + (sp > 1 ? align256(static_cast<size_t>(sp) * cap * d->d_model * 4) : 0);
+  size_t o = w.part + (sp > 1 ? align256(static_cast<size_t>(sp) * cap * d->d_model * 4) : 0);
+  w.row_total = o;   o += align256(T * 4);
+  w.block_total = o; o += align256(nblk * 4);
+  w.light = o;       o += align256(T * 4);
+  w.heavy = o;       o += align256(static_cast<size_t>(heavy_cap(d)) * 4);
+  w.split_n = o;     o += 256;
+  w.heavy_part = o;  o += align256(static_cast<size_t>(heavy_groups(d)) * heavy_cap(d) * d->d_model * 4);
+  w.total = o;
   return w;
 }
 
@@ -212,7 +232,14 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
   r.ell_rows = route->ell_rows;
   r.dense_rows = route->dense_rows;
   r.n_rows = route->n_rows;
+  r.row_total = reinterpret_cast<int32_t*>(wsb + hw.row_total);
+  r.block_total = reinterpret_cast<int32_t*>(wsb + hw.block_total);
+  r.light_rows = reinterpret_cast<int32_t*>(wsb + hw.light);
+  r.heavy_rows = reinterpret_cast<int32_t*>(wsb + hw.heavy);
+  r.split_n = reinterpret_cast<int32_t*>(wsb + hw.split_n);
+  r.heavy_cap = heavy_cap(d);
   TWELL_TRY(from_hip(twell::launch_route(r, s)));
+  TWELL_TRY(from_hip(twell::launch_route_split(r, s)));
 
   twell::FusedArgs f{};
   f.x = x;
@@ -222,14 +249,21 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
   f.w_up_t = w_up_t;
   f.w_down = w_down;
   f.y = y;
-  f.rows = route->ell_rows;
-  f.n_rows_dev = route->n_rows + 0;
+  f.rows = r.light_rows;
+  f.n_rows_dev = r.split_n + 0;
   f.T = d->T;
   f.d = d->d_model;
   f.F = d->d_ff;
   f.tile_n = d->tile_n;
   f.C = d->slots;
   TWELL_TRY(from_hip(twell::launch_fused_updown(f, d->dtype, s)));
+  twell::FusedArgs fh = f;  // heavy ELL rows, cut into tile ranges
+  fh.rows = r.heavy_rows;
+  fh.n_rows_dev = r.split_n + 1;
+  fh.groups = heavy_groups(d);
+  fh.part = reinterpret_cast<float*>(wsb + hw.heavy_part);
+  fh.part_rows = r.heavy_cap;
+  TWELL_TRY(from_hip(twell::launch_fused_split(fh, d->dtype, s)));
 
   if (route->max_dense_rows == 0) return TWELL_OK;
   twell::GateUpArgs g{};

@@ -155,7 +155,11 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
  *        ell_rows / dense_rows, n_rows, row_kind.  At most max_dense_rows
  *        rows are kept dense; further dense rows are served (lossily) from
  *        TwELL and counted in n_rows[2].
- *   3.   fused up/down (as twell_ffn_fwd) over ell_rows;
+ *   3.   fused up/down (as twell_ffn_fwd) over ell_rows; ELL rows with far
+ *        more non-zeros than the batch's mean row (> max(2 slots, 2 x mean),
+ *        at most 1024 of them) are cut into tile ranges processed in parallel
+ *        and summed in a fixed order, so their y can differ from
+ *        twell_ffn_fwd's in the last bits (deterministic either way);
  *   4-5. dense gate|up GEMM over the gathered dense rows (h = ReLU(g) * u,
  *        recomputed, kept in ws), then the down GEMM scattered into y.
  * y [T x d_model] is overwritten.  ws: twell_sizes(d, max_dense_rows).ws_hybrid bytes. */

@@ -84,13 +84,23 @@ def test_hybrid_cap_exceeded_routes_rest_to_ell():
 
 
 def test_hybrid_cap_zero_equals_plain_fused():
+    """With no dense rows every row is served from TwELL: rows of ordinary
+    weight equal the plain fused kernel bit for bit; the heavy rows (total
+    non-zeros > max(2 C, 2 x mean), which the hybrid path cuts into tile
+    ranges summed in a fixed order) agree within the bf16 tolerance."""
     w = W.workload(4, T=700)
     r = run_hybrid(w, 0, label="cap=0")
     y2 = torch.empty_like(r["y"])
     x, wu, wd = (dev(r["inp"][k + "_raw"], w.dtype) for k in ("x", "w_up_t", "w_down"))
     T.twell_ffn_fwd(r["desc"], x, r["act"], wu, wd, y2)
     torch.cuda.synchronize()
-    assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
+    tot = r["act"].count.cpu().numpy().clip(min=0).sum(axis=1)
+    heavy = tot > max(2.0 * w.slots, 2.0 * np.float32(tot.sum() / w.T))
+    assert heavy.any() and not heavy.all()
+    light = torch.from_numpy(~heavy).cuda()
+    assert torch.equal(r["y"][light].view(torch.int16), y2[light].view(torch.int16))
+    yh, y2h = host64(r["y"])[heavy], host64(y2)[heavy]
+    assert np.abs(yh - y2h).max() <= 1e-2 * np.abs(y2h).max()
 
 
 def test_hybrid_all_rows_dense():
