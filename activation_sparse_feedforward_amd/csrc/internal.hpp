@@ -141,6 +141,15 @@ struct BwdArgs {
   void* h_d;
   float* dx_part;       // [dx_splits][cap][d] fp32 split-K partials of the dense rows' dx
   int32_t dx_splits;
+  // light / heavy split of the ELL rows for the token pass (as in the hybrid forward)
+  int32_t* row_total;    // [T]
+  int32_t* block_total;  // [ceil(T/256)]
+  int32_t* light_rows;   // [T]
+  int32_t* heavy_rows;   // [heavy_cap]
+  int32_t* split_n;      // [2]
+  int64_t heavy_cap;
+  int32_t groups;        // tile ranges per heavy row
+  float* dx_hpart;       // [groups][heavy_cap][d] fp32 partial dx of the heavy rows
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.

@@ -20,7 +20,14 @@
 //   pos      per block, rows in order, one LDS cursor per neuron -> the
 //            destination of every (row, slot) pair (within one row every
 //            neuron occurs at most once, so a wave's lanes never collide)
-//   token    one wave per ELL row: dx[t] and the pair records {t, dg, du, h}
+//   totals   per row, the sum of its counts; the ELL rows are then split into
+//            light rows and at most heavy_cap heavy ones (row total >
+//            max(2 C, 2 x mean)), as in the hybrid forward
+//   token    light rows: 16-wave workgroups walking the tiles in lockstep
+//            (x[t], dy[t] in LDS, one row per wave; the weight rows of the
+//            current tiles are shared through L2); heavy rows: one wave per
+//            (row, tile range) with fp32 partial dx reduced in a fixed order;
+//            both write dx[t] and the pair records {t, dg, du, h}
 //   dw       one wave per neuron: walks its pairs in ascending t, fp32 rows
 //            of the three weight gradients in VGPRs, written once.
 #include "common.hpp"
@@ -91,6 +98,33 @@ template <> struct VecB<EF32> {
     return u32x4_t{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
   }
 };
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Per-lane partial dot product of two rows held as NV 16-byte vectors; bf16
+// pairs go through v_dot2c_f32_bf16 (fp32 accumulate) without unpacking, in
+// four interleaved partial sums.  (The 16-byte vector is bit-cast whole to
+// bf16x8 before taking pairs: casting an element of the 32-bit vector directly
+// was compiled to always read element 0.)
+template <class E, int NV>
+__device__ __forceinline__ float row_dot(const u32x4_t* w, const u32x4_t* x) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if constexpr (E::kBytes == 2) {
+      const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w[v]);
+      const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, x[v]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wh[2 * i], wh[2 * i + 1]},
+                                                 bf16x2_t{xh[2 * i], xh[2 * i + 1]}, acc[i], false);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[v][i]), __uint_as_float(x[v][i]), acc[i]);
+    }
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
 
 }  // namespace
 
@@ -201,18 +235,35 @@ __global__ __launch_bounds__(64) void bwd_pos_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------- token pass
-template <class E, int NV>
+// One wave per ELL row (SPLIT = false: every ELL row; used where the lockstep
+// kernel does not fit), or per (heavy row, tile range) with fp32 partial dx
+// written to dx_hpart[range][i][:] (SPLIT = true).
+template <class E, int NV, bool SPLIT>
 __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
   constexpr int kU = NV <= 2 ? 4 : 2;
   __shared__ int4 list_all[kTokWaves][kTokListCap];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kTokWaves + wave;
-  if (i_row >= n_ell_of(p)) return;
-  const int64_t t = p.ell_rows[i_row];
-  int4* list = list_all[wave];
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kTokWaves + wave;
   const int d = p.d, C = p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
+  int64_t i_row = unit;
+  int grp = 0, b_begin = 0, b_end = n_t;
+  int64_t t;
+  if constexpr (SPLIT) {
+    const int64_t n_heavy = min(static_cast<int64_t>(p.split_n[1]), p.heavy_cap);
+    if (unit >= n_heavy * p.groups) return;
+    i_row = unit / p.groups;
+    grp = static_cast<int>(unit - i_row * p.groups);
+    const int tg = (n_t + p.groups - 1) / p.groups;
+    b_begin = min(n_t, grp * tg);
+    b_end = min(n_t, b_begin + tg);
+    t = p.heavy_rows[i_row];
+  } else {
+    if (i_row >= n_ell_of(p)) return;
+    t = p.ell_rows[i_row];
+  }
+  int4* list = list_all[wave];
 
   u32x4_t xs[NV], dys[NV];
   float dxf[NV][kN];
@@ -228,10 +279,10 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs
     }
   }
   const int chunk_tiles = min(kWave, kTokListCap / C);
-  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+  for (int b0 = b_begin; b0 < b_end; b0 += chunk_tiles) {
     const int b = b0 + lane;
     int cnt = 0;
-    if (lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
+    if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
     const int incl = wave_incl_scan(cnt, lane);
     const int total = __shfl(incl, 63);
     const int off = incl - cnt;
@@ -319,9 +370,158 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs
     }
     __builtin_amdgcn_wave_barrier();
   }
-  u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + t * d * E::kBytes);
+  if constexpr (SPLIT) {
+    float* o = p.dx_hpart + (static_cast<int64_t>(grp) * p.heavy_cap + i_row) * d;
 #pragma unroll
-  for (int v = 0; v < NV; ++v) dxr[v * kWave + lane] = VecB<E>::pack(dxf[v]);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < kN; i += 4)
+        *reinterpret_cast<float4*>(o + (v * kWave + lane) * kN + i) =
+            make_float4(dxf[v][i], dxf[v][i + 1], dxf[v][i + 2], dxf[v][i + 3]);
+  } else {
+    u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + t * d * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) dxr[v * kWave + lane] = VecB<E>::pack(dxf[v]);
+  }
+}
+
+// ---------------------------------------------------------------- token pass, lockstep (light rows)
+// 16 waves, one light row each; x[t] and dy[t] sit in LDS, the fp32 dx row in
+// VGPRs.  Every chunk of tiles starts with a workgroup barrier, so all
+// resident workgroups sweep the neurons in roughly the same order and the
+// weight rows (three per active pair) are reused from L2.  The two dot
+// products per pair use packed bf16 pairs (row_dot), so the rounding of u and
+// dh differs in the last bits from bwd_token_kernel's unpacked fp32 sums.
+constexpr int kSyncWavesB = 16;
+constexpr int kSyncListB = 96;  // {j, a, pos} entries per wave per chunk
+
+template <int NV>
+constexpr size_t bwd_sync_lds_bytes() {
+  return static_cast<size_t>(kSyncWavesB) * 2 * NV * kWave * 16 + kSyncWavesB * kSyncListB * 16;
+}
+
+template <class E, int NV>
+__global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(BwdArgs p) {
+  constexpr int kN = VecB<E>::N;
+  constexpr int kRowVec = NV * kWave;
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4_t* xw = reinterpret_cast<u32x4_t*>(smem) + wave * kRowVec;
+  u32x4_t* yw = reinterpret_cast<u32x4_t*>(smem) + (kSyncWavesB + wave) * kRowVec;
+  int4* list = reinterpret_cast<int4*>(smem + kSyncWavesB * 2 * kRowVec * 16) + wave * kSyncListB;
+  const int d = p.d, C = p.C, tile_n = p.tile_n;
+  const int n_t = p.F / tile_n;
+  const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kSyncWavesB + wave;
+  const bool act = i_row < static_cast<int64_t>(p.split_n[0]);  // idle waves still meet every barrier
+  const int64_t t = act ? static_cast<int64_t>(p.light_rows[i_row]) : 0;
+  float dxf[NV][kN];
+  {
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
+    const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      xw[v * kWave + lane] = act ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+      yw[v * kWave + lane] = act ? yr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < kN; ++i) dxf[v][i] = 0.f;
+    }
+  }
+  const int chunk_tiles = max(1, min(kWave, kSyncListB / C));
+  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+    __syncthreads();
+    const int b = b0 + lane;
+    int cnt = 0;
+    if (act && lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
+    const int incl = wave_incl_scan(cnt, lane);
+    const int total = min(__shfl(incl, 63), kSyncListB);
+    const int off = incl - cnt;
+    if (cnt > 0) {
+      const int64_t rec = (t * n_t + b) * C;
+      // off + cnt <= chunk_tiles * C <= kSyncListB
+      for (int s = 0; s < cnt && off + s < kSyncListB; ++s) {
+        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
+        list[off + s] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s)), p.pos[rec + s], 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e = 0; e < total; ++e) {
+      const int4 ent = list[e];
+      const int j = __builtin_amdgcn_readfirstlane(ent.x);
+      const float a = __int_as_float(__builtin_amdgcn_readfirstlane(ent.y));
+      const int pp = __builtin_amdgcn_readfirstlane(ent.z);
+      const int64_t ro = int64_t(j) * d * E::kBytes;
+      const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
+      const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
+      const u32x4_t* gr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_gate_t) + ro);
+      u32x4_t wu[NV], wd[NV], wg[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        wu[v] = ur[v * kWave + lane];
+        wd[v] = dr[v * kWave + lane];
+        wg[v] = gr[v * kWave + lane];
+      }
+      float pu, pe;
+      {
+        u32x4_t xv[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xv[v] = xw[v * kWave + lane];
+        pu = row_dot<E, NV>(wu, xv);
+      }
+      {
+        u32x4_t yv[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) yv[v] = yw[v * kWave + lane];
+        pe = row_dot<E, NV>(wd, yv);
+      }
+      const float u = wave_sum(pu), ee = wave_sum(pe);
+      const float h = a * u;
+      const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+      const float dh = ee + p.l1 * sg;
+      const float du = dh * a;
+      const float dg = dh * u;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float w1[kN], w3[kN];
+        VecB<E>::unpack(wu[v], w1);
+        VecB<E>::unpack(wg[v], w3);
+#pragma unroll
+        for (int i = 0; i < kN; ++i) dxf[v][i] = fmaf(dg, w3[i], fmaf(du, w1[i], dxf[v][i]));
+      }
+      if (lane == 0) p.recs[pp] = make_float4(__int_as_float(static_cast<int>(t)), dg, du, h);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (act) {
+    u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + t * d * E::kBytes);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) dxr[v * kWave + lane] = VecB<E>::pack(dxf[v]);
+  }
+}
+
+// ---------------------------------------------------------------- row totals (for the split)
+__global__ __launch_bounds__(256) void bwd_totals_kernel(BwdArgs p) {
+  __shared__ int wtot[4];
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int n_t = p.F / p.tile_n;
+  int total = 0;
+  if (t < p.T) {
+    for (int b = 0; b < n_t; ++b) total += max(p.count[t * n_t + b], 0);
+    p.row_total[t] = total;
+  }
+  int st = total;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) st += __shfl_xor(st, o);
+  if ((threadIdx.x & 63) == 0) wtot[threadIdx.x >> 6] = st;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    p.block_total[blockIdx.x] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    if (blockIdx.x == 0) {
+      p.split_n[0] = 0;
+      p.split_n[1] = 0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- per-neuron weight gradients
@@ -405,9 +605,48 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
   if (nblk) {
     hipLaunchKernelGGL(bwd_pos_kernel, dim3(nblk, nchunk), dim3(64), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_token_kernel<E, NV>), dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)),
-                       dim3(kTokWaves * kWave), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (NV <= 4) {
+      // light rows in lockstep, heavy rows cut into tile ranges
+      const unsigned tblk = static_cast<unsigned>((a.T + 255) / 256);
+      hipLaunchKernelGGL(bwd_totals_kernel, dim3(tblk), dim3(256), 0, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      RouteArgs r{};
+      r.T = a.T;
+      r.C = a.C;
+      r.ell_rows = const_cast<int32_t*>(a.ell_rows);
+      r.n_rows = const_cast<int32_t*>(a.n_rows);
+      r.row_total = a.row_total;
+      r.block_total = a.block_total;
+      r.light_rows = a.light_rows;
+      r.heavy_rows = a.heavy_rows;
+      r.split_n = a.split_n;
+      r.heavy_cap = a.heavy_cap;
+      if ((e = launch_route_split(r, s)) != hipSuccess) return e;
+      constexpr size_t lds = bwd_sync_lds_bytes<NV>();
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&bwd_token_sync_kernel<E, NV>), hipFuncAttributeMaxDynamicSharedMemorySize,
+          static_cast<int>(lds));
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL((bwd_token_sync_kernel<E, NV>),
+                         dim3(static_cast<unsigned>((a.T + kSyncWavesB - 1) / kSyncWavesB)),
+                         dim3(kSyncWavesB * kWave), lds, s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const int64_t units = a.heavy_cap * a.groups;
+      if (units > 0) {
+        hipLaunchKernelGGL((bwd_token_kernel<E, NV, true>),
+                           dim3(static_cast<unsigned>((units + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave),
+                           0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = launch_splitk_reduce(a.dx_hpart, a.groups, a.heavy_cap, a.split_n + 1, a.heavy_rows, a.dx, a.d,
+                                 E::kBytes == 2 ? 1 : 0, s);
+        if (e != hipSuccess) return e;
+      }
+    } else {
+      hipLaunchKernelGGL((bwd_token_kernel<E, NV, false>),
+                         dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0,
+                         s, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL((bwd_dw_kernel<E, NV>), dim3(static_cast<unsigned>((a.F + 3) / 4)), dim3(4 * kWave), 0, s, a);
   return hipGetLastError();

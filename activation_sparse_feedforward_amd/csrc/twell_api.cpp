@@ -93,7 +93,8 @@ HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
 
 // Workspace layout of the backward.
 struct BwdWs {
-  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, dx_part, total;
+  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, dx_part, row_total, block_total, light, heavy,
+      split_n, dx_hpart, total;
 };
 BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   BwdWs w{};
@@ -112,6 +113,12 @@ BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   w.h_d = o;        o += align256(cap * F * eb);
   const int sp = dense_splits(d);
   w.dx_part = o;    o += sp > 1 ? align256(static_cast<size_t>(sp) * cap * static_cast<size_t>(d->d_model) * 4) : 0;
+  w.row_total = o;  o += align256(T * 4);
+  w.block_total = o; o += align256(((T + 255) / 256) * 4);
+  w.light = o;      o += align256(T * 4);
+  w.heavy = o;      o += align256(static_cast<size_t>(heavy_cap(d)) * 4);
+  w.split_n = o;    o += 256;
+  w.dx_hpart = o;   o += align256(static_cast<size_t>(heavy_groups(d)) * heavy_cap(d) * d->d_model * 4);
   w.total = o;
   return w;
 }
@@ -349,6 +356,14 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.h_d = wsb + bw.h_d;
   a.dx_splits = dense_splits(d);
   a.dx_part = reinterpret_cast<float*>(wsb + bw.dx_part);
+  a.row_total = reinterpret_cast<int32_t*>(wsb + bw.row_total);
+  a.block_total = reinterpret_cast<int32_t*>(wsb + bw.block_total);
+  a.light_rows = reinterpret_cast<int32_t*>(wsb + bw.light);
+  a.heavy_rows = reinterpret_cast<int32_t*>(wsb + bw.heavy);
+  a.split_n = reinterpret_cast<int32_t*>(wsb + bw.split_n);
+  a.heavy_cap = heavy_cap(d);
+  a.groups = heavy_groups(d);
+  a.dx_hpart = reinterpret_cast<float*>(wsb + bw.dx_hpart);
   TWELL_TRY(from_hip(twell::launch_bwd_sparse(a, d->dtype, s)));
   return from_hip(twell::launch_bwd_dense(a, d->dtype, s));
 }
