@@ -321,9 +321,80 @@ def train_step(T, W, args, steps, warmup):
     ph = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i in range(3)]
     n_rows = route.n_rows.cpu().tolist()
     tot = sum(ph)
-    return {"workload": w.name, "ms_per_step": round(tot, 4), "tokens_per_s": round(w.T / tot * 1e3, 1),
-            "phases_ms": {"pack": round(ph[0], 4), "hybrid_fwd": round(ph[1], 4), "bwd": round(ph[2], 4)},
-            "n_ell": n_rows[0], "n_dense": n_rows[1], "dense_over_cap": n_rows[2]}
+    # peak device memory of one step above what is resident before it (inputs, weights, outputs)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    run()
+    torch.cuda.synchronize()
+    twell_peak = torch.cuda.max_memory_allocated() - base
+    # what the forward keeps for the backward: the TwELL planes and the route (x is an input)
+    saved = sz["count"] + sz["idx"] + sz["val"] + 4 * (max(w.T, 1) + cap + 3) + max(w.T, 1)
+    out = {"workload": w.name, "ms_per_step": round(tot, 4), "tokens_per_s": round(w.T / tot * 1e3, 1),
+           "phases_ms": {"pack": round(ph[0], 4), "hybrid_fwd": round(ph[1], 4), "bwd": round(ph[2], 4)},
+           "n_ell": n_rows[0], "n_dense": n_rows[1], "dense_over_cap": n_rows[2],
+           "saved_activation_bytes": int(saved), "workspace_bytes": int(sz["ws_hybrid"] + sz["ws_bwd"]),
+           "step_peak_extra_bytes": int(twell_peak)}
+    if not args.no_dense:
+        out["dense_torch_matmul"] = dense_train_torch(x, wg, wu, wd, dy, w.l1_coef, steps, warmup, stream)
+        out["speedup_vs_dense_train"] = round(out["dense_torch_matmul"]["ms_per_step"] / tot, 3)
+        out["saved_activation_ratio"] = round(saved / out["dense_torch_matmul"]["saved_activation_bytes"], 4)
+    return out
+
+
+def dense_train_torch(x, wg, wu, wd, dy, l1, steps, warmup, stream):
+    """Dense FFN layer training step (forward keeping g and u, backward of the
+    same loss sum(y*dy) + l1*sum|h|) through torch.matmul, i.e. hipBLASLt GEMMs
+    with their native transposed-operand modes: the comparator of the TwELL
+    training step.  bf16 operands, fp32 accumulation, bf16 outputs (dW too)."""
+    import numpy as np
+    import torch
+
+    def fwd():
+        g = torch.matmul(x, wg.t())
+        u = torch.matmul(x, wu.t())
+        a = torch.relu(g)
+        h = a * u
+        return g, u, torch.matmul(h, wd)
+
+    def bwd(g, u):
+        a = torch.relu(g)
+        h = a * u
+        dh = torch.matmul(dy, wd.t()) + l1 * torch.sign(h)
+        du = dh * a
+        dg = dh * u * (g > 0)
+        dx = torch.matmul(dg, wg) + torch.matmul(du, wu)
+        return dx, torch.matmul(dg.t(), x), torch.matmul(du.t(), x), torch.matmul(h.t(), dy)
+
+    def run():
+        g, u, _ = fwd()
+        return bwd(g, u)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        g, u, _ = fwd()
+        ev[k][1].record(stream)
+        bwd(g, u)
+        ev[k][2].record(stream)
+        del g, u
+    torch.cuda.synchronize()
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    r = run()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    del r
+    T_, F_ = x.shape[0], wg.shape[0]
+    flops = 2.0 * T_ * x.shape[1] * F_ * 3 * 3  # 3 GEMMs forward, 6 backward, each 2*T*d*F
+    return {"ms_per_step": round(f_ms + b_ms, 4), "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "tflops": round(flops / (f_ms + b_ms) / 1e9, 1),
+            "saved_activation_bytes": int(2 * T_ * F_ * x.element_size()), "step_peak_extra_bytes": int(peak)}
 
 
 def main():

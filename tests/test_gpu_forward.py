@@ -98,6 +98,7 @@ CASES = [
     ("c5 T=16", W.workload(5, T=16)),
     ("T=1", W.workload(2, T=1)),
     ("c4 lognormal tail", W.workload(4, T=520)),
+    ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
 ]
 
 
@@ -153,6 +154,7 @@ DENSE_CASES = [
     ("c2 ragged", W.workload(2, T=700)),
     ("c3 shape", W.workload(3, T=300)),
     ("rho 5%", W.workload(5, T=260, rho=0.05)),
+    ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
 ]
 
 
