@@ -384,6 +384,145 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   }
 }
 
+// Small-batch variant (few tokens, d_model up to 2048): one workgroup of 16
+// waves per token, the waves splitting the token's tiles into 16 ranges, so a
+// batch of T tokens keeps T workgroups busy instead of T/32.  Each wave walks
+// its range like fused_updown_kernel; the 16 fp32 partial rows meet in LDS
+// and are summed in ascending range order (deterministic) before y[t] is
+// written once.
+constexpr int kTokWaves = 16;
+constexpr int kTokList = 128;  // list entries per wave per chunk
+
+template <int NV, int EB>
+constexpr size_t token_lds_bytes() {
+  return static_cast<size_t>(kTokWaves) * kTokList * 8 + static_cast<size_t>(kTokWaves) * NV * kWave * (16 / EB) * 4 +
+         static_cast<size_t>(NV) * kWave * 16;
+}
+
+template <class E, int NV>
+__global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(FusedArgs p) {
+  constexpr int kN = Vec<E>::N;
+  constexpr int kU = NV <= 2 ? 4 : (NV <= 4 ? 2 : 1);
+  constexpr int kRow = NV * kWave * kN;  // d_model
+  extern __shared__ __align__(16) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int2* list = reinterpret_cast<int2*>(smem) + wave * kTokList;
+  float* ypart = reinterpret_cast<float*>(smem + kTokWaves * kTokList * 8);  // [16][d]
+  u32x4_t* xl = reinterpret_cast<u32x4_t*>(ypart + kTokWaves * kRow);       // x[t], shared by the waves
+  const int64_t i_row = blockIdx.x;
+  const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
+  if (i_row >= n_rows) return;  // uniform over the workgroup, before any barrier
+  const int64_t t = p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row;
+  const int d = p.d, C = p.C, tile_n = p.tile_n;
+  const int n_t = p.F / tile_n;
+  const int tg = (n_t + kTokWaves - 1) / kTokWaves;
+  const int b_begin = min(n_t, wave * tg), b_end = min(n_t, b_begin + tg);
+
+  float yf[NV][kN];
+  {
+    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
+    for (int v = threadIdx.x; v < NV * kWave; v += kTokWaves * kWave) xl[v] = xr[v];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < kN; ++i) yf[v][i] = 0.f;
+  }
+  __syncthreads();
+  const int chunk_tiles = max(1, min(kWave, kTokList / C));
+  for (int b0 = b_begin; b0 < b_end; b0 += chunk_tiles) {
+    const int b = b0 + lane;
+    int cnt = 0;
+    if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
+    const int incl = wave_incl_scan(cnt, lane);
+    const int total = min(__shfl(incl, 63), kTokList);
+    const int off = incl - cnt;
+    if (cnt > 0) {
+      const int64_t rec = (t * n_t + b) * C;
+      for (int s = 0; s < cnt && off + s < kTokList; ++s) {
+        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
+        list[off + s] = make_int2(j, __float_as_int(load_elem<E>(p.val, rec + s)));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int e0 = 0; e0 < total; e0 += kU) {
+      int jj[kU];
+      float aa[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int2 ent = list[min(e0 + q, total - 1)];
+        jj[q] = __builtin_amdgcn_readfirstlane(ent.x);
+        aa[q] = (e0 + q < total) ? __int_as_float(__builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
+      }
+      const int nq = min(kU, total - e0);
+      u32x4_t wu[kU][NV], wd[kU][NV];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int64_t ro = int64_t(jj[q]) * d * E::kBytes;
+        const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
+        const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
+        if (q < nq) {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            wu[q][v] = ur[v * kWave + lane];
+            wd[q][v] = dr[v * kWave + lane];
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) wu[q][v] = wd[q][v] = u32x4_t{0, 0, 0, 0};
+        }
+      }
+      float hq[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        u32x4_t xv[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xv[v] = xl[v * kWave + lane];
+        hq[q] = aa[q] * wave_sum(lane_dot<E, NV>(wu[q], xv));
+      }
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          float w[kN];
+          Vec<E>::unpack(wd[q][v], w);
+#pragma unroll
+          for (int i = 0; i < kN; ++i) yf[v][i] = fmaf(hq[q], w[i], yf[v][i]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  // partial rows -> LDS, then a fixed-order sum over the 16 ranges
+  float* mine = ypart + wave * kRow;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int i = 0; i < kN; i += 4)
+      *reinterpret_cast<float4*>(mine + (v * kWave + lane) * kN + i) =
+          make_float4(yf[v][i], yf[v][i + 1], yf[v][i + 2], yf[v][i + 3]);
+  __syncthreads();
+  for (int e = threadIdx.x; e < kRow; e += kTokWaves * kWave) {
+    float acc = ypart[e];
+#pragma unroll
+    for (int w = 1; w < kTokWaves; ++w) acc += ypart[w * kRow + e];
+    store_bits<E>(p.y, t * d + e, round_store<E>(acc).bits);
+  }
+}
+
+template <class E, int NV>
+static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
+  constexpr size_t lds = token_lds_bytes<NV, E::kBytes>();
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&fused_updown_token_kernel<E, NV>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((fused_updown_token_kernel<E, NV>), dim3(static_cast<unsigned>(a.T)), dim3(kTokWaves * kWave),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
 template <int NV, int TPW, int EB>
 constexpr size_t sync_lds_bytes() {
   return static_cast<size_t>(kSyncWaves) * TPW * NV * kWave * 16 + kSyncWaves * kSyncList * 8;
@@ -451,9 +590,29 @@ hipError_t launch_fused_split(const FusedArgs& a, int dtype, hipStream_t s) {
   return launch_splitk_reduce(a.part, a.groups, a.part_rows, a.n_rows_dev, a.rows, a.y, a.d, dtype, s);
 }
 
+// Batches below this many tokens use the one-workgroup-per-token kernel (the
+// lockstep kernel would keep fewer than T/32 workgroups busy).
+constexpr int64_t kSmallBatch = 2048;
+
 template <class E>
 static hipError_t launch_fused_e(const FusedArgs& a, hipStream_t s) {
   const int nv = a.d / (kWave * Vec<E>::N);
+  if (a.T < kSmallBatch && a.d <= 2048) {
+    switch (nv) {  // d_model <= 2048: NV <= 4 in bf16, <= 8 in fp32
+      case 1: return launch_token_t<E, 1>(a, s);
+      case 2: return launch_token_t<E, 2>(a, s);
+      case 3: return launch_token_t<E, 3>(a, s);
+      case 4: return launch_token_t<E, 4>(a, s);
+      default:
+        if constexpr (E::kBytes == 4) {
+          if (nv == 5) return launch_token_t<E, 5>(a, s);
+          if (nv == 6) return launch_token_t<E, 6>(a, s);
+          if (nv == 7) return launch_token_t<E, 7>(a, s);
+          if (nv == 8) return launch_token_t<E, 8>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
+  }
   switch (nv) {
     case 1: return launch_sync_t<E, 1>(a, s);
     case 2: return launch_sync_t<E, 2>(a, s);

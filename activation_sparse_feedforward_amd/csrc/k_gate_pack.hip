@@ -13,7 +13,8 @@
 // wide stores.
 //
 // T_n = 128 uses the 256 x 256 direct-to-LDS core (gemm256.hpp); T_n = 64 the
-// 256 x 64 register-staged core (gemm_core.hpp).
+// 256 x 64 register-staged core (gemm_core.hpp); batches of at most 64 tokens
+// (bf16, T_n = 128) a kernel that streams W_gate once (gate_pack_small_kernel).
 #include <algorithm>
 
 #include "gemm256.hpp"
@@ -363,8 +364,157 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Small batches (T <= 64, bf16, T_n = 128): the work is reading W_gate once, so
+// the tiling is turned around.  One workgroup per TwELL tile (128 neurons),
+// 4 waves of 32 neurons each; the neurons are the MFMA's M side and the tokens
+// its N side (two 32-token blocks).  With only F/128 workgroups, each must keep
+// a lot of its weight stream in flight: 128-byte K slices of the 128 weight
+// rows (16 KB) and of the 64 token rows (8 KB) move global -> LDS with direct
+// loads through a ring of kSmallStages stages, and the wait before using a
+// slice lets the younger stages stay in flight.  ReLU(g), rounded to bf16, is
+// then staged in LDS as [token][128] and each wave packs a quarter of the
+// tokens: lane l holds columns 2l, 2l + 1, and ballots give the slots in
+// ascending column order.  Same stored values and format as the large-batch
+// kernels.
+constexpr int kSmallT = 64;
+constexpr int kSmallStages = 6;
+constexpr int kSmallStage = (128 + 64) * 128;                   // W slice + x slice
+constexpr int kSmallLds = kSmallStages * kSmallStage;           // 144 KB; the pack reuses it
+
+__global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
+  extern __shared__ __align__(16) char lds[];
+  __shared__ uint32_t ovf_s, nnz_s;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31;
+  const int b = blockIdx.x;  // TwELL tile
+  const int n_t = p.F / 128;
+  const int T = static_cast<int>(p.T);
+  if (threadIdx.x == 0) {
+    ovf_s = 0;
+    nnz_s = 0;
+  }
+  // direct-load sources: instruction q of wave w fills stage rows 8*(4q + w) + lane/8,
+  // rows 0..127 = weight rows, 128..191 = token rows (clamped to T - 1)
+  const char* src[6];
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    const int r = 8 * (4 * q + wave) + (lane >> 3);
+    const int c = (lane & 7) ^ lds_swz(r);
+    const char* base = r < 128 ? static_cast<const char*>(p.w_gate_t) +
+                                     (static_cast<int64_t>(b) * 128 + r) * p.d * 2
+                               : static_cast<const char*>(p.x) + static_cast<int64_t>(min(r - 128, T - 1)) * p.d * 2;
+    src[q] = base + c * 16;
+  }
+  auto issue = [&](int kt) {
+    char* st = lds + (kt % kSmallStages) * kSmallStage;
+#pragma unroll
+    for (int q = 0; q < 6; ++q)
+      __builtin_amdgcn_global_load_lds(src[q] + static_cast<int64_t>(kt) * 128, st + (4 * q + wave) * 8 * 128, 16,
+                                       0, 0);
+  };
+  const int nk = p.d / 64;  // 128-byte slices; d is a multiple of 512
+  const bool two = T > 32;
+  f32x16_t acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+#pragma unroll
+  for (int q = 0; q < kSmallStages - 1; ++q)
+    if (q < nk) issue(q);
+  for (int kt = 0; kt < nk; ++kt) {
+    // slice kt landed when at most the (kSmallStages - 2) younger slices' loads are outstanding
+    if (kt + kSmallStages - 1 <= nk)
+      asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // 4 x 6 loads
+    else
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    // the stage refilled now was last read in iteration kt - 1, which every
+    // wave finished before the barrier above
+    if (kt + kSmallStages - 1 < nk) issue(kt + kSmallStages - 1);
+    const char* st = lds + (kt % kSmallStages) * kSmallStage;
+    Frag<EBf16> fa[4], fb0[4], fb1[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      read_frag256(fa[kk], st, wave * 32 + li, kk, lane);
+      read_frag256(fb0[kk], st, 128 + li, kk, lane);
+      read_frag256(fb1[kk], st, 160 + li, kk, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      mfma_k16(acc0, fa[kk], fb0[kk]);
+      if (two) mfma_k16(acc1, fa[kk], fb1[kk]);
+    }
+  }
+  __syncthreads();  // all loads done, every wave past its last reads: reuse the ring
+  uint16_t(*gl)[128] = reinterpret_cast<uint16_t(*)[128]>(lds);  // [64][128]
+  // acc register r of lane l: neuron 32*wave + acc_row(r, l), token (block) l % 32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int col = wave * 32 + acc_row(r, lane);
+    const float g0 = acc0[r], g1 = acc1[r];
+    if (li < T) gl[li][col] = static_cast<uint16_t>(round_store<EBf16>(g0 > 0.f ? g0 : 0.f).bits);
+    if (two && 32 + li < T) gl[32 + li][col] = static_cast<uint16_t>(round_store<EBf16>(g1 > 0.f ? g1 : 0.f).bits);
+  }
+  __syncthreads();
+  // pack: wave w takes tokens w, w + 4, ...; lane l holds columns 2l and 2l + 1
+  const int C = p.C;
+  uint32_t ovf = 0, nnz = 0;
+  for (int t = wave; t < T; t += 4) {
+    const uint32_t v0 = gl[t][2 * lane], v1 = gl[t][2 * lane + 1];
+    if (p.gate_dbg) {
+      uint16_t* gd = static_cast<uint16_t*>(p.gate_dbg) + static_cast<int64_t>(t) * p.F + b * 128 + 2 * lane;
+      gd[0] = static_cast<uint16_t>(v0);
+      gd[1] = static_cast<uint16_t>(v1);
+    }
+    const int nz0 = v0 != 0u, nz1 = v1 != 0u;
+    const uint64_t m1 = __builtin_amdgcn_ballot_w64(nz0 + nz1 >= 1);
+    const uint64_t m2 = __builtin_amdgcn_ballot_w64(nz0 + nz1 >= 2);
+    const int excl = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m1 >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m1), 0u))) +
+                     static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m2 >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m2), 0u)));
+    const int count = static_cast<int>(__popcll(m1) + __popcll(m2));
+    const int64_t unit = static_cast<int64_t>(t) * n_t + b;
+    const int64_t rec = unit * C;
+    if (lane == 0) p.count[unit] = count;
+    if (nz0 && excl < C) {
+      p.idx[rec + excl] = static_cast<uint8_t>(2 * lane);
+      static_cast<uint16_t*>(p.val)[rec + excl] = static_cast<uint16_t>(v0);
+    }
+    if (nz1 && excl + nz0 < C) {
+      p.idx[rec + excl + nz0] = static_cast<uint8_t>(2 * lane + 1);
+      static_cast<uint16_t*>(p.val)[rec + excl + nz0] = static_cast<uint16_t>(v1);
+    }
+    for (int sl = lane; sl < C; sl += 64)  // slots past the stored entries: (0, +0)
+      if (sl >= count) {
+        p.idx[rec + sl] = 0;
+        static_cast<uint16_t*>(p.val)[rec + sl] = 0;
+      }
+    ovf += count > C ? 1u : 0u;
+    nnz += static_cast<uint32_t>(count);
+  }
+  if (p.stats) {
+    if (lane == 0) {
+      atomicAdd(&ovf_s, ovf);
+      atomicAdd(&nnz_s, nnz);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (ovf_s) atomicAdd(p.stats + 0, static_cast<unsigned long long>(ovf_s));
+      if (nnz_s) atomicAdd(p.stats + 1, static_cast<unsigned long long>(nnz_s));
+    }
+  }
+}
+
+static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(gate_pack_small_kernel, dim3(a.F / 128), dim3(256), kSmallLds, s, a);
+  return hipGetLastError();
+}
+
 template <class E>
 static hipError_t launch_pack_e(const PackArgs& a, hipStream_t s) {
+  if (E::kBytes == 2 && a.tile_n == 128 && a.T <= kSmallT) return launch_pack_small(a, s);
   const bool dbg = a.gate_dbg != nullptr;
   if (a.tile_n == 128) return dbg ? launch_pack256_t<E, true>(a, s) : launch_pack256_t<E, false>(a, s);
   return dbg ? launch_pack64_t<E, true>(a, s) : launch_pack64_t<E, false>(a, s);

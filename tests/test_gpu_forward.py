@@ -12,6 +12,8 @@ Checks per case:
     FFN wherever no tile overflows;
   * dense FFN: y within the same tolerance of the oracle's dense FFN.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -99,6 +101,10 @@ CASES = [
     ("T=1", W.workload(2, T=1)),
     ("c4 lognormal tail", W.workload(4, T=520)),
     ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
+    # batches of 2048+ tokens take the lockstep fused kernel (smaller ones the per-token kernel)
+    ("lockstep ragged T=2049", W.workload(2, T=2049)),
+    ("lockstep C=T_n T=2080", dataclasses.replace(W.workload(2, T=2080, rho=0.3), slots=128)),
+    ("lockstep c4 tail T=2100", W.workload(4, T=2100)),
 ]
 
 
