@@ -256,7 +256,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 // token the arithmetic is exactly that of fused_updown_kernel (same order), so
 // results are bitwise identical.
 constexpr int kSyncWaves = 16;
-constexpr int kSyncList = 256;  // list entries per wave per chunk (8 bytes each)
+constexpr int kSyncList = 128;  // list entries per wave per chunk
+constexpr int kSyncChunkMax = 4;
 
 template <class E, int NV, int TPW, int kU>
 __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
@@ -264,11 +265,11 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
   extern __shared__ __align__(16) char smem[];
   u32x4_t* xl = reinterpret_cast<u32x4_t*>(smem);  // [16 waves][TPW][kRowVec]
-  int2* list_all = reinterpret_cast<int2*>(smem + kSyncWaves * TPW * kRowVec * 16);
+  int4* list_all = reinterpret_cast<int4*>(smem + kSyncWaves * TPW * kRowVec * 16);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
-  int2* list = list_all + wave * kSyncList;
+  int4* list = list_all + wave * kSyncList;
   u32x4_t* xw = xl + wave * TPW * kRowVec;
   const int d = p.d, C = p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
@@ -290,7 +291,9 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     }
   }
   // lanes of the list builder: lane = tile_in_chunk * TPW + token
-  const int chunk_tiles = max(1, min(kWave / TPW, kSyncList / (C * TPW)));
+  // at most 4 tiles per chunk: the weight rows of a chunk (4 x 128 neurons x
+  // 2 rows x d_model x 2 B = 4 MB at d_model = 2048) then fit an XCD's L2
+  const int chunk_tiles = max(1, min(min(kWave / TPW, kSyncList / (C * TPW)), kSyncChunkMax));
   for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
     __syncthreads();
     const int b = b0 + lane / TPW, kl = lane % TPW;
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       // off + cnt <= chunk_tiles * TPW * C <= kSyncList by the launch's choice of TPW
       for (int s = 0; s < cnt && off + s < kSyncList; ++s) {
         const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
-        list[off + s] = make_int2(j | (kl << 28), __float_as_int(load_elem<E>(p.val, rec + s)));
+        list[off + s] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s)), kl, 0);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -322,11 +325,10 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       float aa[kU];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        const int2 ent = list[min(e0 + q, total - 1)];
-        const int jk = __builtin_amdgcn_readfirstlane(ent.x);
-        jj[q] = jk & ((1 << 28) - 1);
+        const int4 ent = list[min(e0 + q, total - 1)];
+        jj[q] = __builtin_amdgcn_readfirstlane(ent.x);
         aa[q] = (q < nq) ? __int_as_float(__builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
-        kk[q] = jk >> 28;
+        kk[q] = __builtin_amdgcn_readfirstlane(ent.z);
       }
       u32x4_t wu[kU][NV], wd[kU][NV];
 #pragma unroll
@@ -525,7 +527,7 @@ static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
 
 template <int NV, int TPW, int EB>
 constexpr size_t sync_lds_bytes() {
-  return static_cast<size_t>(kSyncWaves) * TPW * NV * kWave * 16 + kSyncWaves * kSyncList * 8;
+  return static_cast<size_t>(kSyncWaves) * TPW * NV * kWave * 16 + kSyncWaves * kSyncList * 16;
 }
 
 template <class E, int NV, int TPW, int kU>

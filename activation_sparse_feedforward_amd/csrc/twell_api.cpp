@@ -24,7 +24,6 @@ twell_status check_desc(const twell_desc* d) {
   if (d->d_ff % d->tile_n != 0) return TWELL_EINVAL;
   if (d->slots > d->tile_n) return TWELL_EINVAL;
   if (d->tile_n != 64 && d->tile_n != 128) return TWELL_EUNSUPPORTED;
-  if (d->d_ff >= (1 << 24)) return TWELL_EUNSUPPORTED;  // neuron ids travel in 28-bit fields
   if (d->dtype == TWELL_BF16) {
     if (d->d_model % 512 != 0 || d->d_model > 4096) return TWELL_EUNSUPPORTED;
   } else {

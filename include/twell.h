@@ -42,8 +42,8 @@
  *    reported in device counters, never as host errors.
  *  - Supported shapes: dtype BF16 with d_model % 512 == 0 and d_model <= 4096,
  *    or FP32 with d_model % 256 == 0 and d_model <= 2048; tile_n in {64, 128};
- *    d_ff % tile_n == 0 and d_ff < 2^24; 1 <= slots <= tile_n; T >= 0
- *    (T == 0 is a no-op); T * max(d_model, d_ff) < 2^31.
+ *    d_ff % tile_n == 0; 1 <= slots <= tile_n; T >= 0 (T == 0 is a no-op);
+ *    T * max(d_model, d_ff) < 2^31.
  *  - Threading: calls are thread-safe (no global mutable state).
  */
 #ifndef TWELL_H
