@@ -68,7 +68,8 @@ struct RouteArgs {
   int32_t* block_total;  // [ceil(T/256)] sum of row_total per block
   int32_t* light_rows;   // [T]
   int32_t* heavy_rows;   // [heavy_cap]
-  int32_t* split_n;      // [2] {n_light, n_heavy (may exceed heavy_cap: clamp)}
+  int32_t* split_n;      // [2] {n_light, n_heavy}
+  int32_t* block_heavy;  // [ceil(T/256)] heavy rows per block of list positions
   int64_t heavy_cap;
 };
 
@@ -147,6 +148,7 @@ struct BwdArgs {
   int32_t* light_rows;   // [T]
   int32_t* heavy_rows;   // [heavy_cap]
   int32_t* split_n;      // [2]
+  int32_t* block_heavy;  // [ceil(T/256)]
   int64_t heavy_cap;
   int32_t groups;        // tile ranges per heavy row
   float* dx_hpart;       // [groups][heavy_cap][d] fp32 partial dx of the heavy rows

@@ -517,10 +517,6 @@ __global__ __launch_bounds__(256) void bwd_totals_kernel(BwdArgs p) {
   __syncthreads();
   if (threadIdx.x == 0) {
     p.block_total[blockIdx.x] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    if (blockIdx.x == 0) {
-      p.split_n[0] = 0;
-      p.split_n[1] = 0;
-    }
   }
 }
 
@@ -620,6 +616,7 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
       r.light_rows = a.light_rows;
       r.heavy_rows = a.heavy_rows;
       r.split_n = a.split_n;
+      r.block_heavy = a.block_heavy;
       r.heavy_cap = a.heavy_cap;
       if ((e = launch_route_split(r, s)) != hipSuccess) return e;
       constexpr size_t lds = bwd_sync_lds_bytes<NV>();

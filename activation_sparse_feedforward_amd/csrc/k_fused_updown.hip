@@ -253,8 +253,9 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 // XCD's L2 instead of each wave fetching random rows from the MALL; more
 // tokens per workgroup keeps the workgroups in tighter step.  x[t] lives in
 // LDS (this frees the VGPRs for the fp32 y accumulators of TPW tokens).  Per
-// token the arithmetic is exactly that of fused_updown_kernel (same order), so
-// results are bitwise identical.
+// token the arithmetic is that of fused_updown_kernel, with the tiles summed
+// starting from the workgroup's rotated chunk (a function of the workgroup
+// index, so results are deterministic for a given row list).
 constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
@@ -294,7 +295,13 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   // at most 4 tiles per chunk: the weight rows of a chunk (4 x 128 neurons x
   // 2 rows x d_model x 2 B = 4 MB at d_model = 2048) then fit an XCD's L2
   const int chunk_tiles = max(1, min(min(kWave / TPW, kSyncList / (C * TPW)), kSyncChunkMax));
-  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+  // Workgroups are dealt round-robin to the 8 XCDs; each XCD's workgroups start
+  // their sweep at a different chunk (and wrap around), so the XCDs do not all
+  // request the same weight rows from the MALL at the same time.
+  const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
+  const int rot = static_cast<int>(blockIdx.x & 7) * (n_chunks / 8);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int b0 = ((c + rot) % n_chunks) * chunk_tiles;
     __syncthreads();
     const int b = b0 + lane / TPW, kl = lane % TPW;
     int cnt = 0;

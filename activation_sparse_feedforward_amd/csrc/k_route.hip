@@ -105,10 +105,6 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(RouteArgs p)
     }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (p.split_n) {  // launch_route_split appends to these after this kernel
-      p.split_n[0] = 0;
-      p.split_n[1] = 0;
-    }
     const int64_t total = sum_upto;
     const int64_t kept = total < p.cap ? total : p.cap;
     p.n_rows[0] = static_cast<int32_t>(p.T - kept);
@@ -117,13 +113,20 @@ __global__ __launch_bounds__(kRouteBlock) void route_scatter_kernel(RouteArgs p)
   }
 }
 
-// One thread per ELL-list position.  Heavy rows (many more non-zeros than the
-// batch's mean row) would hold a lockstep workgroup of the fused kernel back
-// at every chunk barrier; they are listed apart (up to heavy_cap; any excess
-// stays light) and cut into tile ranges by launch_fused_split.  Appends use
-// one atomic per wave and category, so the lists are in no particular order
-// (every row's own arithmetic does not depend on it).
-__global__ __launch_bounds__(kRouteBlock) void route_split_kernel(RouteArgs p) {
+// Split of the ELL list into light rows and at most heavy_cap heavy rows (row
+// total > max(2 C, 2 x the batch's mean row total)).  Heavy rows would hold a
+// lockstep workgroup of the fused kernel back at every chunk barrier; they are
+// cut into tile ranges by launch_fused_split.  Both lists keep the ascending
+// order of ell_rows (so everything downstream is deterministic): per block of
+// 256 list positions, split_count counts the heavy rows and split_scatter
+// places every row from the count of heavy rows before it (earlier blocks +
+// in-block scan); heavy rows past the cap stay light.
+__device__ __forceinline__ bool is_heavy_row(const RouteArgs& p, int64_t i, float mean) {
+  const float thr = fmaxf(2.f * p.C, 2.f * mean);
+  return static_cast<float>(p.row_total[p.ell_rows[i]]) > thr;
+}
+
+__device__ __forceinline__ float batch_mean_total(const RouteArgs& p) {
   __shared__ float s_mean;
   const int nblk = static_cast<int>((p.T + kRouteBlock - 1) / kRouteBlock);
   if (threadIdx.x == 0) {
@@ -132,40 +135,74 @@ __global__ __launch_bounds__(kRouteBlock) void route_split_kernel(RouteArgs p) {
     s_mean = p.T > 0 ? static_cast<float>(static_cast<double>(tot) / static_cast<double>(p.T)) : 0.f;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
+  return s_mean;
+}
+
+__global__ __launch_bounds__(kRouteBlock) void route_split_count_kernel(RouteArgs p) {
+  __shared__ int wsum[kRouteBlock / kWave];
+  const float mean = batch_mean_total(p);
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
+  const int h = (i < p.n_rows[0] && is_heavy_row(p, i, mean)) ? 1 : 0;
+  int sum = h;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) p.block_heavy[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+__global__ __launch_bounds__(kRouteBlock) void route_split_scatter_kernel(RouteArgs p) {
+  __shared__ int red[kRouteBlock / kWave];
+  __shared__ int wpre[kRouteBlock / kWave];
+  const float mean = batch_mean_total(p);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n_ell = p.n_rows[0];
+  const int nblk = static_cast<int>((p.T + kRouteBlock - 1) / kRouteBlock);
+  // heavy rows in earlier blocks (block 0 also totals every block)
+  const int upto = blockIdx.x == 0 ? nblk : static_cast<int>(blockIdx.x);
+  int part = 0;
+  for (int b = threadIdx.x; b < upto; b += kRouteBlock) part += p.block_heavy[b];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  const int sum_upto = red[0] + red[1] + red[2] + red[3];
+  const int64_t before_block = blockIdx.x == 0 ? 0 : sum_upto;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kRouteBlock + threadIdx.x;
   const bool live = i < n_ell;
-  int32_t t = 0;
-  bool heavy = false;
-  if (live) {
-    t = p.ell_rows[i];
-    const float thr = fmaxf(2.f * p.C, 2.f * s_mean);
-    heavy = static_cast<float>(p.row_total[t]) > thr;
+  const int h = (live && is_heavy_row(p, i, mean)) ? 1 : 0;
+  int incl = h;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
   }
-  // heavy appends first; slots past the cap fall back to the light list
-  const uint64_t mh = __builtin_amdgcn_ballot_w64(live && heavy);
-  int hbase = 0;
-  if (lane == 0 && mh) hbase = atomicAdd(p.split_n + 1, static_cast<int>(__popcll(mh)));
-  hbase = __shfl(hbase, 0);
-  const int hslot = hbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mh >> 32),
-                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mh), 0u)));
-  const bool to_heavy = live && heavy && hslot < p.heavy_cap;
-  if (to_heavy) p.heavy_rows[hslot] = t;
-  const bool to_light = live && !to_heavy;
-  const uint64_t ml = __builtin_amdgcn_ballot_w64(to_light);
-  int lbase = 0;
-  if (lane == 0 && ml) lbase = atomicAdd(p.split_n + 0, static_cast<int>(__popcll(ml)));
-  lbase = __shfl(lbase, 0);
-  const int lslot = lbase + static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ml >> 32),
-                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ml), 0u)));
-  if (to_light) p.light_rows[lslot] = t;
+  if (lane == 63) wpre[wave] = incl;
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += wpre[w];
+  const int64_t heavy_before = before_block + wave_off + incl - h;
+  if (live) {
+    const int32_t t = p.ell_rows[i];
+    if (h && heavy_before < p.heavy_cap)
+      p.heavy_rows[heavy_before] = t;
+    else
+      p.light_rows[i - min(heavy_before, p.heavy_cap)] = t;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int64_t kept = min(static_cast<int64_t>(sum_upto), p.heavy_cap);
+    p.split_n[0] = static_cast<int32_t>(n_ell - kept);
+    p.split_n[1] = static_cast<int32_t>(kept);
+  }
 }
 
 hipError_t launch_route_split(const RouteArgs& a, hipStream_t s) {
   const unsigned nblk = static_cast<unsigned>((a.T + kRouteBlock - 1) / kRouteBlock);
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_split_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
+  hipLaunchKernelGGL(route_split_count_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_split_scatter_kernel, dim3(nblk), dim3(kRouteBlock), 0, s, a);
   return hipGetLastError();
 }
 

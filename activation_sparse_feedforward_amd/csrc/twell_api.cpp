@@ -68,7 +68,7 @@ int heavy_groups(const twell_desc* d) {
 // lists, their counters) and the heavy rows' partial outputs
 // [groups x heavy_cap x d_model] fp32.
 struct HybridWs {
-  size_t block_dense, h, part, row_total, block_total, light, heavy, split_n, heavy_part, total;
+  size_t block_dense, h, part, row_total, block_total, block_heavy, light, heavy, split_n, heavy_part, total;
 };
 HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
   HybridWs w{};
@@ -82,6 +82,7 @@ HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
   size_t o = w.part + (sp > 1 ? align256(static_cast<size_t>(sp) * cap * d->d_model * 4) : 0);
   w.row_total = o;   o += align256(T * 4);
   w.block_total = o; o += align256(nblk * 4);
+  w.block_heavy = o; o += align256(nblk * 4);
   w.light = o;       o += align256(T * 4);
   w.heavy = o;       o += align256(static_cast<size_t>(heavy_cap(d)) * 4);
   w.split_n = o;     o += 256;
@@ -92,8 +93,8 @@ HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
 
 // Workspace layout of the backward.
 struct BwdWs {
-  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, dx_part, row_total, block_total, light, heavy,
-      split_n, dx_hpart, total;
+  size_t blk_hist, neuron_off, pos, recs, g_d, u_d, dg_d, du_d, h_d, dx_part, row_total, block_total, block_heavy,
+      light, heavy, split_n, dx_hpart, total;
 };
 BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   BwdWs w{};
@@ -114,6 +115,7 @@ BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   w.dx_part = o;    o += sp > 1 ? align256(static_cast<size_t>(sp) * cap * static_cast<size_t>(d->d_model) * 4) : 0;
   w.row_total = o;  o += align256(T * 4);
   w.block_total = o; o += align256(((T + 255) / 256) * 4);
+  w.block_heavy = o; o += align256(((T + 255) / 256) * 4);
   w.light = o;      o += align256(T * 4);
   w.heavy = o;      o += align256(static_cast<size_t>(heavy_cap(d)) * 4);
   w.split_n = o;    o += 256;
@@ -243,6 +245,7 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
   r.light_rows = reinterpret_cast<int32_t*>(wsb + hw.light);
   r.heavy_rows = reinterpret_cast<int32_t*>(wsb + hw.heavy);
   r.split_n = reinterpret_cast<int32_t*>(wsb + hw.split_n);
+  r.block_heavy = reinterpret_cast<int32_t*>(wsb + hw.block_heavy);
   r.heavy_cap = heavy_cap(d);
   TWELL_TRY(from_hip(twell::launch_route(r, s)));
   TWELL_TRY(from_hip(twell::launch_route_split(r, s)));
@@ -360,6 +363,7 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.light_rows = reinterpret_cast<int32_t*>(wsb + bw.light);
   a.heavy_rows = reinterpret_cast<int32_t*>(wsb + bw.heavy);
   a.split_n = reinterpret_cast<int32_t*>(wsb + bw.split_n);
+  a.block_heavy = reinterpret_cast<int32_t*>(wsb + bw.block_heavy);
   a.heavy_cap = heavy_cap(d);
   a.groups = heavy_groups(d);
   a.dx_hpart = reinterpret_cast<float*>(wsb + bw.dx_hpart);

@@ -120,3 +120,19 @@ def test_hybrid_full_size_sampled():
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([np.arange(256), np.arange(w.T - 256, w.T), rng.choice(w.T, 256, replace=False)]))
     run_hybrid(w, 1024, rows=rows, label="full c4")
+
+
+def test_hybrid_deterministic_lockstep():
+    """A batch large enough for the lockstep fused kernel (whose chunk order
+    depends on the workgroup), with heavy and dense rows: two calls give the
+    same bits."""
+    w = W.workload(4, T=2600)
+    rows = np.arange(0, w.T, 13)
+    r = run_hybrid(w, 128, rows=rows, label="determinism a")
+    x, wg, wu, wd = (dev(r["inp"][k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
+    ws = torch.empty(T.sizes(r["desc"], 128)["ws_hybrid"], dtype=torch.uint8, device="cuda")
+    route2 = T.alloc_route(r["desc"], 128)
+    y2 = poison_(torch.empty_like(r["y"]))
+    T.twell_ffn_fwd_hybrid(r["desc"], x, wg, r["act"], wu, wd, y2, route2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
