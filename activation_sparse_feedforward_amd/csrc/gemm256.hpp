@@ -12,7 +12,8 @@
 //    ways).  Rows past the matrix are clamped to its last row: they only
 //    feed output rows/columns that the epilogues discard.
 //  * Two LDS stages (2 x 64 KB): the loads of slice k+1 fly while slice k is
-//    multiplied; one barrier per slice.
+//    multiplied; one barrier per slice; the slice body interleaves loads and
+//    fragment reads with the MFMAs (see gemm256_mainloop).
 //  * Tile order is XCD-aware: consecutive workgroup ids are dealt round-robin
 //    to the 8 XCDs, so ids are remapped to give every XCD a contiguous run of
 //    tiles, walked in groups of 8 M tiles so that the workgroups resident on
@@ -87,12 +88,15 @@ struct DirectRows {
       ptr[q] = static_cast<const char*>(second ? base2 : base) + gr * ld * E::kBytes + c * 16;
     }
   }
-  __device__ __forceinline__ void issue(int kt, char* lds_tile) const {
-    const int wave = threadIdx.x >> 6;
+  // One wave instruction (round q) of K slice kt; wave_u is the wave index as a
+  // wave-uniform value, so the LDS destination (M0) needs no readfirstlane.
+  __device__ __forceinline__ void issue_one(int kt, char* lds_tile, int q, int wave_u) const {
+    __builtin_amdgcn_global_load_lds(ptr[q] + static_cast<int64_t>(kt) * 128, lds_tile + (q * 32 + wave_u * 8) * 128,
+                                     16, 0, 0);
+  }
+  __device__ __forceinline__ void issue(int kt, char* lds_tile, int wave_u) const {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds(ptr[q] + static_cast<int64_t>(kt) * 128,
-                                       lds_tile + (q * 32 + wave * 8) * 128, 16, 0, 0);
+    for (int q = 0; q < 8; ++q) issue_one(kt, lds_tile, q, wave_u);
   }
 };
 
@@ -110,16 +114,24 @@ __device__ __forceinline__ void read_frag256(Frag<EF32>& f, const char* lds, int
 }
 
 // nk K slices of 128 bytes.  lds: kLds256 bytes, 16-byte aligned.
-// Fragment reads are software-pipelined: the reads of k-step kk+1 are issued
-// before the MFMAs of k-step kk, so with one wave per SIMD the matrix core is
-// not left waiting on LDS latency between k-steps.  The per-slice barrier is a
-// bare s_barrier after an explicit wait for this wave's direct loads (HIP's
-// __syncthreads would also wait for every load in flight).
+//
+// With one wave per SIMD, any run of non-MFMA instructions leaves the matrix
+// core idle, so the slice body is scheduled by hand (sched_barrier after each
+// step pins the order): every MFMA of k-step kk is followed by at most one
+// fragment read for k-step kk+1 and, in k-step 0, by one of the 16 direct
+// loads of the next slice.  Issued in clumps, the same instructions cost a
+// fifth of the loop's cycles.  The last slice re-loads itself into the idle
+// stage (keeps the body branch-free); the final vmcnt wait makes sure no
+// direct load is still writing LDS when the caller reuses it or the
+// workgroup ends.  One barrier per slice, after an explicit wait for this
+// wave's direct loads (HIP's __syncthreads would also wait for every load in
+// flight).
 template <class E>
 __device__ __forceinline__ void gemm256_mainloop(const DirectRows<E>& la, const DirectRows<E>& lb, int nk,
                                                  char* lds, Acc256& acc) {
   constexpr int kSteps = 128 / E::kBytes / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int arow = (wave >> 1) * 128 + (lane & 31);
   const int brow = (wave & 1) * 128 + (lane & 31);
 #pragma unroll
@@ -129,38 +141,43 @@ __device__ __forceinline__ void gemm256_mainloop(const DirectRows<E>& la, const 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.f;
   if (nk <= 0) return;
-  la.issue(0, lds);
-  lb.issue(0, lds + kT256 * 128);
+  la.issue(0, lds, wave_u);
+  lb.issue(0, lds + kT256 * 128, wave_u);
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = lds + (kt & 1) * kStageBytes;
+    const int kl = kt + 1 < nk ? kt + 1 : kt;
+    const char* A = lds + (kt & 1) * kStageBytes;
+    const char* B = A + kT256 * 128;
     char* nxt = lds + ((kt + 1) & 1) * kStageBytes;
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const char* A = cur;
-    const char* B = cur + kT256 * 128;
     Frag<E> a[2][4], b[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) read_frag256(a[0][i], A, arow + i * 32, 0, lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j) read_frag256(b[0][j], B, brow + j * 32, 0, lane);
-    if (kt + 1 < nk) {
-      la.issue(kt + 1, nxt);
-      lb.issue(kt + 1, nxt + kT256 * 128);
-    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < kSteps; ++kk) {
       const int cb = kk & 1;
-      if (kk + 1 < kSteps) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) read_frag256(a[cb ^ 1][i], A, arow + i * 32, kk + 1, lane);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) read_frag256(b[cb ^ 1][j], B, brow + j * 32, kk + 1, lane);
+      for (int m = 0; m < 16; ++m) {
+        mfma_k16(acc.c[m >> 2][m & 3], a[cb][m >> 2], b[cb][m & 3]);
+        if (kk + 1 < kSteps && m < 8) {
+          if (m < 4)
+            read_frag256(a[cb ^ 1][m], A, arow + m * 32, kk + 1, lane);
+          else
+            read_frag256(b[cb ^ 1][m - 4], B, brow + (m - 4) * 32, kk + 1, lane);
+        }
+        if (kk == 0) {
+          if (m < 8)
+            la.issue_one(kl, nxt, m, wave_u);
+          else
+            lb.issue_one(kl, nxt + kT256 * 128, m - 8, wave_u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mfma_k16(acc.c[i][j], a[cb][i], b[cb][j]);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace twell
