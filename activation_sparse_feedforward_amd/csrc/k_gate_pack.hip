@@ -144,16 +144,26 @@ __device__ __forceinline__ void pack_epilogue(const PackArgs& p, const f32x16_t 
 // lane l of accumulator block j holds tile column 4*l + j, so each lane holds 4
 // consecutive columns of a row, and a row's ascending column order is lane
 // order, then j.  One register index r covers 2 rows x 128 columns (lanes 0-31:
-// row ra, lanes 32-63: row ra + 4).  A non-zero's slot is the exclusive prefix,
-// over the lanes of its half, of the per-lane non-zero counts c (0..4), plus
-// its rank inside the lane; the prefix is built from the ballots of c >= k
-// (k = 1..4; prefix(c) = sum_k prefix([c >= k])), where lanes with two or more
-// non-zeros are rare enough to sit behind a uniform branch.  Records are
-// assembled in LDS exactly as in pack_epilogue.  The statistics (overflowing
-// tiles, non-zeros) are computed from the final counts, and only when asked.
-// Row counts are parked in LDS as they are produced (lanes 0 and 32 write the
-// two rows of a register), which keeps 32 scalar counts from piling up in SGPRs.
-// kC > 0 fixes C at compile time (record offsets become immediates); 0 reads p.C.
+// row ra, lanes 32-63: row ra + 4).
+//
+// With one wave per SIMD this code is bound by instruction issue, so the
+// common case is short and branch-free.  "Stored value is non-zero" is a
+// signed compare of the fp32 bits, so per lane the largest and the second
+// largest bit pattern of its four values tell whether it holds any, and
+// whether it holds two or more, non-zeros.  Registers with no non-zero at all
+// are skipped.  When no lane holds two or more (one uniform test), a row's
+// count is the popcount of the "lane has a non-zero" mask over its half, a
+// non-zero's slot is that mask's exclusive prefix (mbcnt), its value is the
+// lane's largest, and every lane writes one index byte and one value, lanes
+// with nothing to store (or past C) into a private dummy slot.  Registers
+// where some lane holds two or more non-zeros take a general path: the prefix
+// over the per-lane counts c (0..4) is built from the ballots of c >= k,
+// k = 1..4.
+// Records are assembled in LDS exactly as in pack_epilogue; the counts go
+// into lane i < 32 of one register (row i) with v_writelane.  The statistics
+// (overflowing tiles, non-zeros) are computed from the final counts, and only
+// when asked.  kC > 0 fixes C at compile time (record offsets become
+// immediates); 0 reads p.C.
 // wlds: pack_lc_scratch_bytes(C, sizeof(dtype)) bytes, 16-byte aligned.
 template <class E, bool DBG, int kC>
 __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16_t (&acc)[4][4], int64_t wrow0,
@@ -166,64 +176,91 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
   const int idx_bytes = C, val_bytes = C * E::kBytes;
   uint8_t* l_idx = reinterpret_cast<uint8_t*>(wlds);
   char* l_val = wlds + 32 * idx_bytes;
-  const int rec_words = 32 * (idx_bytes + val_bytes) / 4;
-  int* l_cnt = reinterpret_cast<int*>(wlds + ((32 * (idx_bytes + val_bytes) + 15) & ~15));
+  const int rec_bytes = 32 * (idx_bytes + val_bytes);  // a multiple of 16
+  uint8_t* dummy_idx = reinterpret_cast<uint8_t*>(wlds + rec_bytes) + lane;
+  char* dummy_val = wlds + rec_bytes + 64 + lane * E::kBytes;
+  const uint32_t half_mask = half ? 0xffffffffu : 0u;
   const int piece = (C % 16) == 0 ? 16 : ((C % 4) == 0 ? 4 : 1);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    for (int i = lane; i < rec_words; i += 64) reinterpret_cast<uint32_t*>(wlds)[i] = 0u;
+    for (int i = lane; i < rec_bytes / 16; i += 64) reinterpret_cast<u32x4_t*>(wlds)[i] = u32x4_t{0u, 0u, 0u, 0u};
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t row0 = wrow0 + mb * 32;
+    int cnt_v = 0;  // lane i < 32: count of row row0 + i
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ra = 8 * (r >> 2) + (r & 3);
       const int rr = ra + 4 * half;
-      uint32_t u[4];
-      int bits = 0;
+      int u[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u[j] = __float_as_uint(acc[mb][j][r]);
-        bits |= (static_cast<int>(u[j]) >= kNzMin ? 1 : 0) << j;
-      }
+      for (int j = 0; j < 4; ++j) u[j] = __float_as_int(acc[mb][j][r]);
       if constexpr (DBG) {
         const int64_t row = row0 + rr;
         if (row < p.T)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             store_bits<E>(p.gate_dbg, row * p.F + static_cast<int64_t>(b) * 128 + 4 * li + j,
-                          (bits >> j) & 1 ? round_store<E>(__uint_as_float(u[j])).bits : 0u);
+                          u[j] >= kNzMin ? round_store<E>(__int_as_float(u[j])).bits : 0u);
       }
-      const uint64_t m1 = __builtin_amdgcn_ballot_w64(bits != 0);
-      int pre_a = 0, pre_b = 0;
-      if (m1 != 0) {
-        const int c = __popc(bits);
-        const uint32_t lo1 = static_cast<uint32_t>(m1), hi1 = static_cast<uint32_t>(m1 >> 32);
-        pre_a = __popc(lo1);
-        pre_b = __popc(hi1);
-        int excl = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi1, __builtin_amdgcn_mbcnt_lo(lo1, 0u))) -
-                   (half ? pre_a : 0);
-        const uint64_t m2 = __builtin_amdgcn_ballot_w64(c >= 2);
-        if (m2 != 0) {
+      // The test "stored value is non-zero" is a signed compare of the fp32
+      // bits, so the largest and second largest bit patterns of the lane's four
+      // values say whether it holds one, or two or more, non-zeros.
+      const int top3 = max(max(u[0], u[1]), u[2]);
+      const int big = max(top3, u[3]);
+      const uint64_t any = __builtin_amdgcn_ballot_w64(big >= kNzMin);
+      if (any == 0) continue;
+      const int med3 = max(min(u[0], u[1]), min(max(u[0], u[1]), u[2]));
+      const int second = max(med3, min(top3, u[3]));
+      const uint64_t two = __builtin_amdgcn_ballot_w64(second >= kNzMin);
+      const uint32_t lo1 = static_cast<uint32_t>(any), hi1 = static_cast<uint32_t>(any >> 32);
+      const int excl1 = static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi1, __builtin_amdgcn_mbcnt_lo(lo1, 0u))) -
+                        static_cast<int>(static_cast<uint32_t>(__popc(lo1)) & half_mask);
+      if (__builtin_expect(two == 0, 1)) {
+        // at most one non-zero per lane, and it is the largest value
+        const int pre_a = __popc(lo1), pre_b = __popc(hi1);
+        asm("v_writelane_b32 %0, %1, %2" : "+v"(cnt_v) : "s"(pre_a), "i"(ra));
+        asm("v_writelane_b32 %0, %1, %2" : "+v"(cnt_v) : "s"(pre_b), "i"(ra + 4));
+        const int jj = u[0] >= kNzMin ? 0 : (u[1] >= kNzMin ? 1 : (u[2] >= kNzMin ? 2 : 3));
+        const bool ok = big >= kNzMin && excl1 < C;
+        uint8_t* ia = ok ? l_idx + rr * idx_bytes + excl1 : dummy_idx;
+        char* va = ok ? l_val + rr * val_bytes + excl1 * E::kBytes : dummy_val;
+        *ia = static_cast<uint8_t>(4 * li + jj);
+        const uint32_t vb = round_store<E>(__int_as_float(big)).bits;
+        if constexpr (E::kBytes == 2)
+          *reinterpret_cast<uint16_t*>(va) = static_cast<uint16_t>(vb);
+        else
+          *reinterpret_cast<uint32_t*>(va) = vb;
+      } else {
+        bool nz[4];
+        int pre_a = 0, pre_b = 0;
 #pragma unroll
-          for (int k = 2; k <= 4; ++k) {
-            const uint64_t mk = __builtin_amdgcn_ballot_w64(c >= k);
-            const uint32_t lo = static_cast<uint32_t>(mk), hi = static_cast<uint32_t>(mk >> 32);
-            const int plo = __popc(lo);
-            excl += static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))) -
-                    (half ? plo : 0);
-            pre_a += plo;
-            pre_b += __popc(hi);
-          }
+        for (int j = 0; j < 4; ++j) {
+          nz[j] = u[j] >= kNzMin;
+          const uint64_t mj = __builtin_amdgcn_ballot_w64(nz[j]);
+          pre_a += __popc(static_cast<uint32_t>(mj));
+          pre_b += __popc(static_cast<uint32_t>(mj >> 32));
+        }
+        asm("v_writelane_b32 %0, %1, %2" : "+v"(cnt_v) : "s"(pre_a), "i"(ra));
+        asm("v_writelane_b32 %0, %1, %2" : "+v"(cnt_v) : "s"(pre_b), "i"(ra + 4));
+        const int bits = (nz[0] ? 1 : 0) | (nz[1] ? 2 : 0) | (nz[2] ? 4 : 0) | (nz[3] ? 8 : 0);
+        const int c = __popc(bits);
+        int excl = excl1;
+#pragma unroll
+        for (int k = 2; k <= 4; ++k) {
+          const uint64_t mk = __builtin_amdgcn_ballot_w64(c >= k);
+          const uint32_t lo = static_cast<uint32_t>(mk), hi = static_cast<uint32_t>(mk >> 32);
+          excl += static_cast<int>(__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u))) -
+                  static_cast<int>(static_cast<uint32_t>(__popc(lo)) & half_mask);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if ((bits >> j) & 1) {
+          if (nz[j]) {
             const int s = excl + __popc(bits & ((1 << j) - 1));
             if (s < C) {
               l_idx[rr * idx_bytes + s] = static_cast<uint8_t>(4 * li + j);
-              const uint32_t vb = round_store<E>(__uint_as_float(u[j])).bits;
+              const uint32_t vb = round_store<E>(__int_as_float(u[j])).bits;
               if constexpr (E::kBytes == 2)
                 reinterpret_cast<uint16_t*>(l_val + rr * val_bytes)[s] = static_cast<uint16_t>(vb);
               else
@@ -232,12 +269,10 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
           }
         }
       }
-      if (li == 0) l_cnt[rr] = half ? pre_b : pre_a;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int cnt_v = l_cnt[li];  // lane i < 32: count of row row0 + i
     const bool row_ok = lane < 32 && row0 + lane < p.T;
     if (p.stats) {
       const int cv = row_ok ? cnt_v : 0;
@@ -247,9 +282,6 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
       for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
       nnz += static_cast<uint32_t>(__shfl(sum, 0));
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (row_ok) p.count[(row0 + lane) * n_t + b] = cnt_v;
     const int ip = idx_bytes / piece, vp = val_bytes / piece;
     for (int w = lane; w < 32 * (ip + vp); w += 64) {
@@ -281,7 +313,8 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
 
 // Bytes of LDS scratch one wave's epilogue needs.
 __host__ __device__ constexpr int pack_scratch_bytes(int C, int eb) { return ((32 * C * (1 + eb)) + 15) & ~15; }
-__host__ __device__ constexpr int pack_lc_scratch_bytes(int C, int eb) { return pack_scratch_bytes(C, eb) + 128; }
+// The lane-column epilogue adds 64 dummy index bytes and 64 dummy values (one per lane).
+__host__ __device__ constexpr int pack_lc_scratch_bytes(int C, int eb) { return pack_scratch_bytes(C, eb) + 64 + 64 * eb; }
 
 // ovf / nnz are wave-uniform (they are built from ballot popcounts), so lane 0
 // publishes the wave's totals.
