@@ -101,6 +101,22 @@ __device__ __forceinline__ float lane_dot(const u32x4_t* w, const u32x4_t* x) {
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
+// One 16-byte piece of lane_dot, accumulated into the same four chains.
+template <class E>
+__device__ __forceinline__ void lane_dot_piece(const u32x4_t& w, const u32x4_t& x, float (&acc)[4]) {
+  if constexpr (E::kBytes == 2) {
+    const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w);
+    const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wh[2 * i], wh[2 * i + 1]}, bf16x2_t{xh[2 * i], xh[2 * i + 1]},
+                                               acc[i], false);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[i]), __uint_as_float(x[i]), acc[i]);
+  }
+}
+
 // Inclusive prefix sum over the wave (Hillis-Steele with shuffles); small and
 // only run once per 64 tiles.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
@@ -260,7 +276,7 @@ constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
 
-template <class E, int NV, int TPW, int kU>
+template <class E, int NV, int TPW, int kU, int kC>
 __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
   constexpr int kN = Vec<E>::N;
   constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
@@ -268,11 +284,11 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   u32x4_t* xl = reinterpret_cast<u32x4_t*>(smem);  // [16 waves][TPW][kRowVec]
   int4* list_all = reinterpret_cast<int4*>(smem + kSyncWaves * TPW * kRowVec * 16);
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
   int4* list = list_all + wave * kSyncList;
   u32x4_t* xw = xl + wave * TPW * kRowVec;
-  const int d = p.d, C = p.C, tile_n = p.tile_n;
+  const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
 
   int64_t tk[TPW];
@@ -282,7 +298,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   for (int k = 0; k < TPW; ++k) {
     const int64_t i_row = (static_cast<int64_t>(blockIdx.x) * kSyncWaves + wave) * TPW + k;
     act[k] = i_row < n_rows;  // idle tokens: the wave still takes part in the barriers
-    tk[k] = act[k] ? (p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row) : 0;
+    // wave-uniform: keep the token rows in scalar registers
+    tk[k] = act[k] ? (p.rows ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.rows[i_row])) : i_row) : 0;
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + tk[k] * d * E::kBytes);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -300,27 +317,64 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   // request the same weight rows from the MALL at the same time.
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
   const int rot = static_cast<int>(blockIdx.x & 7) * (n_chunks / 8);
+  const int kl = lane % TPW;
+  int my_tok = 0;  // token rows are < 2^31
+  bool my_act = false;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k)
+    if (kl == k) {
+      my_tok = static_cast<int>(tk[k]);
+      my_act = act[k] && lane < chunk_tiles * TPW;
+    }
+  // C = 16: the builder lane's count and 16 index bytes of the next chunk are
+  // loaded while the current chunk's entries are processed, so a chunk starts
+  // without waiting on global memory; an entry carries the position of its
+  // value, which is loaded beside the entry's weight rows.
+  int pf_cnt = 0;
+  u32x4_t pf_idx{0, 0, 0, 0};
+  auto prefetch = [&](int c) {
+    const int b = ((c + rot) % n_chunks) * chunk_tiles + lane / TPW;
+    pf_cnt = 0;
+    if (my_act && b < n_t) {
+      const int64_t rec = static_cast<int64_t>(my_tok) * n_t + b;
+      pf_cnt = p.count[rec];
+      pf_idx = *reinterpret_cast<const u32x4_t*>(p.idx + rec * 16);
+    }
+  };
+  if constexpr (kC == 16) prefetch(0);
   for (int c = 0; c < n_chunks; ++c) {
     const int b0 = ((c + rot) % n_chunks) * chunk_tiles;
     __syncthreads();
-    const int b = b0 + lane / TPW, kl = lane % TPW;
-    int cnt = 0;
-    int64_t tl = 0;
+    const int b = b0 + lane / TPW;
+    int total;
+    if constexpr (kC == 16) {
+      const int cnt = max(0, min(pf_cnt, 16));
+      const u32x4_t ix = pf_idx;
+      const int vpos = (my_tok * n_t + b) * 16;
+      const int incl = wave_incl_scan(cnt, lane);
+      total = min(__shfl(incl, 63), kSyncList);
+      const int off = incl - cnt;
 #pragma unroll
-    for (int k = 0; k < TPW; ++k)
-      if (kl == k) {
-        tl = tk[k];
-        if (act[k] && lane < chunk_tiles * TPW && b < n_t) cnt = max(0, min(p.count[tk[k] * n_t + b], C));
+      for (int s2 = 0; s2 < 16; ++s2) {
+        if (s2 < cnt && off + s2 < kSyncList) {
+          const int j = b * tile_n + (static_cast<int>((ix[s2 >> 2] >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
+          list[off + s2] = make_int4(j, vpos + s2, kl, 0);
+        }
       }
-    const int incl = wave_incl_scan(cnt, lane);
-    const int total = min(__shfl(incl, 63), kSyncList);
-    const int off = incl - cnt;
-    if (cnt > 0) {
-      const int64_t rec = (tl * n_t + b) * C;
-      // off + cnt <= chunk_tiles * TPW * C <= kSyncList by the launch's choice of TPW
-      for (int s = 0; s < cnt && off + s < kSyncList; ++s) {
-        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
-        list[off + s] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s)), kl, 0);
+      if (c + 1 < n_chunks) prefetch(c + 1);
+    } else {
+      int cnt = 0;
+      if (my_act && b < n_t) cnt = max(0, min(p.count[static_cast<int64_t>(my_tok) * n_t + b], C));
+      const int incl = wave_incl_scan(cnt, lane);
+      total = min(__shfl(incl, 63), kSyncList);
+      const int off = incl - cnt;
+      if (cnt > 0) {
+        const int64_t rec = (static_cast<int64_t>(my_tok) * n_t + b) * C;
+        // off + cnt <= chunk_tiles * TPW * C <= kSyncList by the launch's choice of TPW
+        for (int s2 = 0; s2 < cnt && off + s2 < kSyncList; ++s2) {
+          const int j = b * tile_n + (p.idx[rec + s2] & (tile_n - 1));
+          list[off + s2] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s2)), kl, 0);
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -334,7 +388,10 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       for (int q = 0; q < kU; ++q) {
         const int4 ent = list[min(e0 + q, total - 1)];
         jj[q] = __builtin_amdgcn_readfirstlane(ent.x);
-        aa[q] = (q < nq) ? __int_as_float(__builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
+        if constexpr (kC == 16)
+          aa[q] = (q < nq) ? load_elem<E>(p.val, __builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
+        else
+          aa[q] = (q < nq) ? __int_as_float(__builtin_amdgcn_readfirstlane(ent.y)) : 0.f;
         kk[q] = __builtin_amdgcn_readfirstlane(ent.z);
       }
       u32x4_t wu[kU][NV], wd[kU][NV];
@@ -357,11 +414,16 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       float hq[kU];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
+        // x comes from LDS one 16-byte piece at a time (keeps 12 VGPRs free)
         const u32x4_t* xq = xw + kk[q] * kRowVec;
-        u32x4_t xv[NV];
+        float acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < NV; ++v) xv[v] = xq[v * kWave + lane];
-        hq[q] = lane_dot<E, NV>(wu[q], xv);
+        for (int v = 0; v < NV; ++v) {
+          const u32x4_t xv = xq[v * kWave + lane];
+          lane_dot_piece<E>(wu[q][v], xv, acc4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        hq[q] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
       }
 #pragma unroll
       for (int q = 0; q < kU; ++q) hq[q] = aa[q] * wave_sum(hq[q]);
@@ -540,13 +602,25 @@ constexpr size_t sync_lds_bytes() {
 template <class E, int NV, int TPW, int kU>
 static hipError_t launch_sync_cfg(const FusedArgs& a, hipStream_t s) {
   constexpr size_t lds = sync_lds_bytes<NV, TPW, E::kBytes>();
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (attr != hipSuccess) return attr;
   const int64_t per_block = static_cast<int64_t>(kSyncWaves) * TPW;
   dim3 grid(static_cast<unsigned>((a.T + per_block - 1) / per_block));
-  hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+  if constexpr (E::kBytes == 2) {
+    if (a.C == 16) {
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 16>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (attr != hipSuccess) return attr;
+      hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 16>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+      return hipGetLastError();
+    }
+  }
+  {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 0>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 0>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+  }
   return hipGetLastError();
 }
 
