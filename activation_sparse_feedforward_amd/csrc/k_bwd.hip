@@ -126,6 +126,22 @@ __device__ __forceinline__ float row_dot(const u32x4_t* w, const u32x4_t* x) {
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
+// One 16-byte piece of row_dot, accumulated into the same four chains.
+template <class E>
+__device__ __forceinline__ void row_dot_piece(const u32x4_t& w, const u32x4_t& x, float (&acc)[4]) {
+  if constexpr (E::kBytes == 2) {
+    const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w);
+    const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wh[2 * i], wh[2 * i + 1]}, bf16x2_t{xh[2 * i], xh[2 * i + 1]},
+                                               acc[i], false);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[i]), __uint_as_float(x[i]), acc[i]);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- hist
@@ -400,20 +416,22 @@ constexpr size_t bwd_sync_lds_bytes() {
   return static_cast<size_t>(kSyncWavesB) * 2 * NV * kWave * 16 + kSyncWavesB * kSyncListB * 16;
 }
 
-template <class E, int NV>
+template <class E, int NV, int kC>
 __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
   constexpr int kRowVec = NV * kWave;
   extern __shared__ __align__(16) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   u32x4_t* xw = reinterpret_cast<u32x4_t*>(smem) + wave * kRowVec;
   u32x4_t* yw = reinterpret_cast<u32x4_t*>(smem) + (kSyncWavesB + wave) * kRowVec;
   int4* list = reinterpret_cast<int4*>(smem + kSyncWavesB * 2 * kRowVec * 16) + wave * kSyncListB;
-  const int d = p.d, C = p.C, tile_n = p.tile_n;
+  const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
   const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kSyncWavesB + wave;
   const bool act = i_row < static_cast<int64_t>(p.split_n[0]);  // idle waves still meet every barrier
-  const int64_t t = act ? static_cast<int64_t>(p.light_rows[i_row]) : 0;
+  // wave-uniform: the token row stays in scalar registers
+  const int64_t t = act ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.light_rows[i_row])) : 0;
   float dxf[NV][kN];
   {
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
@@ -427,20 +445,54 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
     }
   }
   const int chunk_tiles = max(1, min(kWave, kSyncListB / C));
+  // C = 16: the builder lanes load the next chunk's counts and 16 index bytes
+  // while the current chunk's entries are processed; an entry carries its
+  // slot position, from which its value and record position are loaded beside
+  // the weight rows.
+  int pf_cnt = 0;
+  u32x4_t pf_idx{0, 0, 0, 0};
+  auto prefetch = [&](int b0) {
+    const int b = b0 + lane;
+    pf_cnt = 0;
+    if (act && lane < chunk_tiles && b < n_t) {
+      const int64_t rec = t * n_t + b;
+      pf_cnt = p.count[rec];
+      pf_idx = *reinterpret_cast<const u32x4_t*>(p.idx + rec * 16);
+    }
+  };
+  if constexpr (kC == 16) prefetch(0);
   for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
     __syncthreads();
     const int b = b0 + lane;
-    int cnt = 0;
-    if (act && lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
-    const int incl = wave_incl_scan(cnt, lane);
-    const int total = min(__shfl(incl, 63), kSyncListB);
-    const int off = incl - cnt;
-    if (cnt > 0) {
-      const int64_t rec = (t * n_t + b) * C;
-      // off + cnt <= chunk_tiles * C <= kSyncListB
-      for (int s = 0; s < cnt && off + s < kSyncListB; ++s) {
-        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
-        list[off + s] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s)), p.pos[rec + s], 0);
+    int total;
+    if constexpr (kC == 16) {
+      const int cnt = max(0, min(pf_cnt, 16));
+      const u32x4_t ix = pf_idx;
+      const int incl = wave_incl_scan(cnt, lane);
+      total = min(__shfl(incl, 63), kSyncListB);
+      const int off = incl - cnt;
+      const int spos = static_cast<int>((t * n_t + b) * 16);
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        if (s2 < cnt && off + s2 < kSyncListB) {
+          const int j = b * tile_n + (static_cast<int>((ix[s2 >> 2] >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
+          list[off + s2] = make_int4(j, spos + s2, 0, 0);
+        }
+      }
+      if (b0 + chunk_tiles < n_t) prefetch(b0 + chunk_tiles);
+    } else {
+      int cnt = 0;
+      if (act && lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
+      const int incl = wave_incl_scan(cnt, lane);
+      total = min(__shfl(incl, 63), kSyncListB);
+      const int off = incl - cnt;
+      if (cnt > 0) {
+        const int64_t rec = (t * n_t + b) * C;
+        // off + cnt <= chunk_tiles * C <= kSyncListB
+        for (int s2 = 0; s2 < cnt && off + s2 < kSyncListB; ++s2) {
+          const int j = b * tile_n + (p.idx[rec + s2] & (tile_n - 1));
+          list[off + s2] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s2)), p.pos[rec + s2], 0);
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -449,8 +501,16 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
     for (int e = 0; e < total; ++e) {
       const int4 ent = list[e];
       const int j = __builtin_amdgcn_readfirstlane(ent.x);
-      const float a = __int_as_float(__builtin_amdgcn_readfirstlane(ent.y));
-      const int pp = __builtin_amdgcn_readfirstlane(ent.z);
+      float a;
+      int pp;
+      if constexpr (kC == 16) {
+        const int sp = __builtin_amdgcn_readfirstlane(ent.y);
+        a = load_elem<E>(p.val, sp);
+        pp = p.pos[sp];
+      } else {
+        a = __int_as_float(__builtin_amdgcn_readfirstlane(ent.y));
+        pp = __builtin_amdgcn_readfirstlane(ent.z);
+      }
       const int64_t ro = int64_t(j) * d * E::kBytes;
       const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
       const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
@@ -462,19 +522,22 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
         wd[v] = dr[v * kWave + lane];
         wg[v] = gr[v * kWave + lane];
       }
-      float pu, pe;
-      {
-        u32x4_t xv[NV];
+      // x and dy come from LDS one 16-byte piece at a time (fewer live VGPRs)
+      float au[4] = {0.f, 0.f, 0.f, 0.f}, ae[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int v = 0; v < NV; ++v) xv[v] = xw[v * kWave + lane];
-        pu = row_dot<E, NV>(wu, xv);
+      for (int v = 0; v < NV; ++v) {
+        const u32x4_t xv = xw[v * kWave + lane];
+        row_dot_piece<E>(wu[v], xv, au);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      {
-        u32x4_t yv[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) yv[v] = yw[v * kWave + lane];
-        pe = row_dot<E, NV>(wd, yv);
+      for (int v = 0; v < NV; ++v) {
+        const u32x4_t yv = yw[v * kWave + lane];
+        row_dot_piece<E>(wd[v], yv, ae);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      const float pu = (au[0] + au[1]) + (au[2] + au[3]);
+      const float pe = (ae[0] + ae[1]) + (ae[2] + ae[3]);
       const float u = wave_sum(pu), ee = wave_sum(pe);
       const float h = a * u;
       const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
@@ -498,6 +561,23 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
 #pragma unroll
     for (int v = 0; v < NV; ++v) dxr[v * kWave + lane] = VecB<E>::pack(dxf[v]);
   }
+}
+
+template <class E, int NV, int kC>
+static hipError_t launch_bwd_sync_c(const BwdArgs& a, hipStream_t s) {
+  constexpr size_t lds = bwd_sync_lds_bytes<NV>();
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_sync_kernel<E, NV, kC>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((bwd_token_sync_kernel<E, NV, kC>), dim3(static_cast<unsigned>((a.T + kSyncWavesB - 1) / kSyncWavesB)),
+                     dim3(kSyncWavesB * kWave), lds, s, a);
+  return hipGetLastError();
+}
+template <class E, int NV>
+static hipError_t launch_bwd_sync(const BwdArgs& a, hipStream_t s) {
+  if constexpr (E::kBytes == 2)
+    if (a.C == 16) return launch_bwd_sync_c<E, NV, 16>(a, s);
+  return launch_bwd_sync_c<E, NV, 0>(a, s);
 }
 
 // ---------------------------------------------------------------- row totals (for the split)
@@ -619,15 +699,7 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
       r.block_heavy = a.block_heavy;
       r.heavy_cap = a.heavy_cap;
       if ((e = launch_route_split(r, s)) != hipSuccess) return e;
-      constexpr size_t lds = bwd_sync_lds_bytes<NV>();
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&bwd_token_sync_kernel<E, NV>), hipFuncAttributeMaxDynamicSharedMemorySize,
-          static_cast<int>(lds));
-      if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL((bwd_token_sync_kernel<E, NV>),
-                         dim3(static_cast<unsigned>((a.T + kSyncWavesB - 1) / kSyncWavesB)),
-                         dim3(kSyncWavesB * kWave), lds, s, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = launch_bwd_sync<E, NV>(a, s)) != hipSuccess) return e;
       const int64_t units = a.heavy_cap * a.groups;
       if (units > 0) {
         hipLaunchKernelGGL((bwd_token_kernel<E, NV, true>),
