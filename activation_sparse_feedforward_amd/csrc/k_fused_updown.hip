@@ -303,7 +303,10 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + tk[k] * d * E::kBytes);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      xw[k * kRowVec + v * kWave + lane] = act[k] ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+      // x, the counts / indices and y are touched once: non-temporal accesses
+      // keep them from pushing the shared weight rows out of L2
+      xw[k * kRowVec + v * kWave + lane] =
+          act[k] ? __builtin_nontemporal_load(xr + v * kWave + lane) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < kN; ++i) yf[k][v][i] = 0.f;
     }
@@ -337,8 +340,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     pf_cnt = 0;
     if (my_act && b < n_t) {
       const int64_t rec = static_cast<int64_t>(my_tok) * n_t + b;
-      pf_cnt = p.count[rec];
-      pf_idx = *reinterpret_cast<const u32x4_t*>(p.idx + rec * 16);
+      pf_cnt = __builtin_nontemporal_load(p.count + rec);
+      pf_idx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.idx + rec * 16));
     }
   };
   if constexpr (kC == 16) prefetch(0);
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     if (act[k]) {
       u32x4_t* yr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.y) + tk[k] * d * E::kBytes);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) yr[v * kWave + lane] = Vec<E>::pack(yf[k][v]);
+      for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(Vec<E>::pack(yf[k][v]), yr + v * kWave + lane);
     }
   }
 }
