@@ -438,8 +438,10 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
     const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      xw[v * kWave + lane] = act ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
-      yw[v * kWave + lane] = act ? yr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+      // x, dy, the counts / indices and dx are touched once: non-temporal
+      // accesses keep them from pushing the shared weight rows out of L2
+      xw[v * kWave + lane] = act ? __builtin_nontemporal_load(xr + v * kWave + lane) : u32x4_t{0, 0, 0, 0};
+      yw[v * kWave + lane] = act ? __builtin_nontemporal_load(yr + v * kWave + lane) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < kN; ++i) dxf[v][i] = 0.f;
     }
@@ -456,8 +458,8 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
     pf_cnt = 0;
     if (act && lane < chunk_tiles && b < n_t) {
       const int64_t rec = t * n_t + b;
-      pf_cnt = p.count[rec];
-      pf_idx = *reinterpret_cast<const u32x4_t*>(p.idx + rec * 16);
+      pf_cnt = __builtin_nontemporal_load(p.count + rec);
+      pf_idx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.idx + rec * 16));
     }
   };
   if constexpr (kC == 16) prefetch(0);
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
   if (act) {
     u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + t * d * E::kBytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) dxr[v * kWave + lane] = VecB<E>::pack(dxf[v]);
+    for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(VecB<E>::pack(dxf[v]), dxr + v * kWave + lane);
   }
 }
 
