@@ -133,8 +133,8 @@ struct BwdArgs {
   // workspace
   int32_t* blk_hist;    // [ceil(T/64)][F]
   int32_t* neuron_off;  // [F + 1]
-  int32_t* pos;         // [T][n_t][C]
-  float4* recs;         // [T * n_t * C] {t, dg, du, h}
+  int2* pairs;          // [T * n_t * C] neuron-major {t, slot}
+  float2* coef;         // [T][n_t][C] (dg, du) of each stored slot
   float* g_d;           // [cap][F]
   float* u_d;           // [cap][F]
   void* dg_d;           // [cap][F] dtype

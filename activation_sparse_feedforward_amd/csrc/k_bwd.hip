@@ -17,19 +17,26 @@
 //   hist     per block of 64 ELL rows, LDS histogram of neuron ids
 //   colscan  per neuron, exclusive scan over the blocks
 //   nscan    exclusive scan over neurons -> start of each neuron's pair list
-//   pos      per block, rows in order, one LDS cursor per neuron -> the
-//            destination of every (row, slot) pair (within one row every
+//   pos      per block, rows in order, one LDS cursor per neuron -> the pair
+//            list {t, slot} in neuron-major order (within one row every
 //            neuron occurs at most once, so a wave's lanes never collide)
+//   dw       one wave per neuron j: W_up^T[j] and W_down[j] stay in VGPRs
+//            while the wave walks j's pairs in ascending t, gathering x[t] and
+//            dy[t]; it forms u, dh, dg, du, h for each pair, stores (dg, du)
+//            in the pair's TwELL slot and keeps the three fp32 weight-gradient
+//            rows in VGPRs, written once
 //   totals   per row, the sum of its counts; the ELL rows are then split into
 //            light rows and at most heavy_cap heavy ones (row total >
 //            max(2 C, 2 x mean)), as in the hybrid forward
-//   token    light rows: 16-wave workgroups walking the tiles in lockstep
-//            (x[t], dy[t] in LDS, one row per wave; the weight rows of the
-//            current tiles are shared through L2); heavy rows: one wave per
-//            (row, tile range) with fp32 partial dx reduced in a fixed order;
-//            both write dx[t] and the pair records {t, dg, du, h}
-//   dw       one wave per neuron: walks its pairs in ascending t, fp32 rows
-//            of the three weight gradients in VGPRs, written once.
+//   dx       token-major: dx[t] = sum over t's slots of dg W_gate^T[j] +
+//            du W_up^T[j], with (dg, du) read back from the slot.  Light rows:
+//            16-wave workgroups walking the tiles in lockstep, so the weight
+//            rows of the current tiles are shared through L2; heavy rows: one
+//            wave per (row, tile range) with fp32 partial dx reduced in a
+//            fixed order.
+// Per pair each pass gathers two rows (x[t] and dy[t], then W_gate^T[j] and
+// W_up^T[j]), and both dot products sit in the per-neuron pass, where one of
+// their operands is already in registers.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -124,22 +131,6 @@ __device__ __forceinline__ float row_dot(const u32x4_t* w, const u32x4_t* x) {
     }
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
-// One 16-byte piece of row_dot, accumulated into the same four chains.
-template <class E>
-__device__ __forceinline__ void row_dot_piece(const u32x4_t& w, const u32x4_t& x, float (&acc)[4]) {
-  if constexpr (E::kBytes == 2) {
-    const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w);
-    const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, x);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc[i] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_t{wh[2 * i], wh[2 * i + 1]}, bf16x2_t{xh[2 * i], xh[2 * i + 1]},
-                                               acc[i], false);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[i]), __uint_as_float(x[i]), acc[i]);
-  }
 }
 
 }  // namespace
@@ -239,7 +230,7 @@ __global__ __launch_bounds__(64) void bwd_pos_kernel(BwdArgs p) {
           if (j >= 0 && j < nj) {
             const int q = cursor[j];
             cursor[j] = q + 1;
-            p.pos[rec + s] = q;
+            p.pairs[q] = make_int2(static_cast<int>(t), static_cast<int>(rec + s));
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -250,15 +241,124 @@ __global__ __launch_bounds__(64) void bwd_pos_kernel(BwdArgs p) {
   }
 }
 
-// ---------------------------------------------------------------- token pass
+// ---------------------------------------------------------------- per-neuron pass
+// One wave per neuron j.  Its W_up^T and W_down rows are loaded once and stay
+// in VGPRs; for each pair (t, slot) in ascending t the wave gathers x[t] and
+// dy[t] and forms
+//     u = x[t].W_up^T[j], e = dy[t].W_down[j], h = a u, dh = e + l1 sign(h),
+//     du = dh a, dg = dh u
+// (a = the slot's stored ReLU value).  (dg, du) go to the slot for the dx
+// pass; dg x[t], du x[t] and h dy[t] accumulate into fp32 rows in VGPRs.  Up
+// to d_model = 2048 (bf16) two pairs are in flight per iteration.
+template <class E, int NV>
+__global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
+  constexpr int kN = VecB<E>::N;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (j >= p.F) return;
+  const int d = p.d;
+  u32x4_t wu[NV], wd[NV];
+  {
+    const int64_t ro = j * d * E::kBytes;
+    const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
+    const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      // the neuron's own rows are read by this wave only
+      wu[v] = __builtin_nontemporal_load(ur + v * kWave + lane);
+      wd[v] = __builtin_nontemporal_load(dr + v * kWave + lane);
+    }
+  }
+  float ag[NV][kN], au[NV][kN], ad[NV][kN];
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int i = 0; i < kN; ++i) ag[v][i] = au[v][i] = ad[v][i] = 0.f;
+  const int beg = p.neuron_off[j], end = p.neuron_off[j + 1];
+  constexpr int kP = NV <= 4 ? 2 : 1;  // wider rows: one pair at a time, fewer spills
+  for (int e0 = beg; e0 < end; e0 += kP) {
+    float aq[kP];
+    int sq[kP];
+    u32x4_t xv[kP][NV], yv[kP][NV];
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      const bool live = e0 + q < end;
+      const int2 pr = live ? p.pairs[e0 + q] : make_int2(0, 0);
+      sq[q] = pr.y;
+      aq[q] = live ? load_elem<E>(p.val, pr.y) : 0.f;
+      // clamped so that a corrupted pair cannot address outside x / dy
+      const int64_t t = min(max(static_cast<int64_t>(pr.x), int64_t(0)), p.T - 1);
+      const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
+      const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        xv[q][v] = live ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+        yv[q][v] = live ? yr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
+      }
+    }
+    float uq[kP], eq[kP];
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      uq[q] = row_dot<E, NV>(wu, xv[q]);
+      eq[q] = row_dot<E, NV>(wd, yv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      uq[q] = wave_sum(uq[q]);
+      eq[q] = wave_sum(eq[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      // a dead pair has a = 0 and zero rows, so it adds nothing
+      const float a = aq[q], u = uq[q];
+      const float h = a * u;
+      const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+      const float dh = eq[q] + p.l1 * sg;
+      const float du = dh * a;
+      const float dg = dh * u;
+      if (e0 + q < end && lane == 0) p.coef[sq[q]] = make_float2(dg, du);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        float xf[kN], yf[kN];
+        VecB<E>::unpack(xv[q][v], xf);
+        VecB<E>::unpack(yv[q][v], yf);
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+          ag[v][i] = fmaf(dg, xf[i], ag[v][i]);
+          au[v][i] = fmaf(du, xf[i], au[v][i]);
+          ad[v][i] = fmaf(h, yf[i], ad[v][i]);
+        }
+      }
+    }
+  }
+  float* og = p.dw_gate_t + j * d;
+  float* ou = p.dw_up_t + j * d;
+  float* od = p.dw_down + j * d;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int64_t c = static_cast<int64_t>(v * kWave + lane) * kN;
+#pragma unroll
+    for (int i = 0; i < kN; i += 4) {
+      *reinterpret_cast<f32x4_t*>(og + c + i) = f32x4_t{ag[v][i], ag[v][i + 1], ag[v][i + 2], ag[v][i + 3]};
+      *reinterpret_cast<f32x4_t*>(ou + c + i) = f32x4_t{au[v][i], au[v][i + 1], au[v][i + 2], au[v][i + 3]};
+      *reinterpret_cast<f32x4_t*>(od + c + i) = f32x4_t{ad[v][i], ad[v][i + 1], ad[v][i + 2], ad[v][i + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dx pass
+// dx[t] = sum over t's stored slots of dg W_gate^T[j] + du W_up^T[j], with
+// (dg, du) written to the slot by the per-neuron pass.  The tiles are walked in
+// ascending order, so every row's sum has a fixed order.
+
 // One wave per ELL row (SPLIT = false: every ELL row; used where the lockstep
 // kernel does not fit), or per (heavy row, tile range) with fp32 partial dx
 // written to dx_hpart[range][i][:] (SPLIT = true).
 template <class E, int NV, bool SPLIT>
-__global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_ell_dx_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
   constexpr int kU = NV <= 2 ? 4 : 2;
-  __shared__ int4 list_all[kTokWaves][kTokListCap];
+  __shared__ int2 list_all[kTokWaves][kTokListCap];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kTokWaves + wave;
   const int d = p.d, C = p.C, tile_n = p.tile_n;
@@ -279,21 +379,12 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs
     if (i_row >= n_ell_of(p)) return;
     t = p.ell_rows[i_row];
   }
-  int4* list = list_all[wave];
-
-  u32x4_t xs[NV], dys[NV];
+  int2* list = list_all[wave];
   float dxf[NV][kN];
-  {
-    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
-    const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      xs[v] = xr[v * kWave + lane];
-      dys[v] = yr[v * kWave + lane];
+  for (int v = 0; v < NV; ++v)
 #pragma unroll
-      for (int i = 0; i < kN; ++i) dxf[v][i] = 0.f;
-    }
-  }
+    for (int i = 0; i < kN; ++i) dxf[v][i] = 0.f;
   const int chunk_tiles = min(kWave, kTokListCap / C);
   for (int b0 = b_begin; b0 < b_end; b0 += chunk_tiles) {
     const int b = b0 + lane;
@@ -304,84 +395,49 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs
     const int off = incl - cnt;
     if (cnt > 0) {
       const int64_t rec = (t * n_t + b) * C;
-      for (int s = 0; s < cnt; ++s) {
-        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
-        const float a = load_elem<E>(p.val, rec + s);
-        list[off + s] = make_int4(j, __float_as_int(a), p.pos[rec + s], 0);
-      }
+      for (int s = 0; s < cnt; ++s)
+        list[off + s] = make_int2(b * tile_n + (p.idx[rec + s] & (tile_n - 1)), static_cast<int>(rec + s));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
     for (int e0 = 0; e0 < total; e0 += kU) {
       const int nq = min(kU, total - e0);
-      int jj[kU], pp[kU];
-      float aa[kU];
+      int jj[kU];
+      float2 cf[kU];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        const int4 ent = list[min(e0 + q, total - 1)];
+        const int2 ent = list[min(e0 + q, total - 1)];
         jj[q] = __builtin_amdgcn_readfirstlane(ent.x);
-        aa[q] = __int_as_float(__builtin_amdgcn_readfirstlane(ent.y));
-        pp[q] = __builtin_amdgcn_readfirstlane(ent.z);
+        cf[q] = q < nq ? p.coef[__builtin_amdgcn_readfirstlane(ent.y)] : make_float2(0.f, 0.f);
       }
-      u32x4_t wu[kU][NV], wd[kU][NV], wg[kU][NV];
+      u32x4_t wg[kU][NV], wu[kU][NV];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
         const int64_t ro = int64_t(jj[q]) * d * E::kBytes;
-        const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
-        const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
         const u32x4_t* gr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_gate_t) + ro);
+        const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
         if (q < nq) {
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
-            wu[q][v] = ur[v * kWave + lane];
-            wd[q][v] = dr[v * kWave + lane];
             wg[q][v] = gr[v * kWave + lane];
+            wu[q][v] = ur[v * kWave + lane];
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < NV; ++v) wu[q][v] = wd[q][v] = wg[q][v] = u32x4_t{0, 0, 0, 0};
+          for (int v = 0; v < NV; ++v) wg[q][v] = wu[q][v] = u32x4_t{0, 0, 0, 0};
         }
-      }
-      float uu[kU], ee[kU];
-#pragma unroll
-      for (int q = 0; q < kU; ++q) {
-        float pu = 0.f, pe = 0.f;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          float w1[kN], w2[kN], xv[kN], yv[kN];
-          VecB<E>::unpack(wu[q][v], w1);
-          VecB<E>::unpack(wd[q][v], w2);
-          VecB<E>::unpack(xs[v], xv);
-          VecB<E>::unpack(dys[v], yv);
-#pragma unroll
-          for (int i = 0; i < kN; ++i) {
-            pu = fmaf(xv[i], w1[i], pu);
-            pe = fmaf(yv[i], w2[i], pe);
-          }
-        }
-        uu[q] = wave_sum(pu);
-        ee[q] = wave_sum(pe);
       }
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        const float a = q < nq ? aa[q] : 0.f;
-        const float h = a * uu[q];
-        const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-        const float dh = ee[q] + p.l1 * sg;
-        const float du = dh * a;
-        const float dg = q < nq ? dh * uu[q] : 0.f;
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           float w1[kN], w3[kN];
           VecB<E>::unpack(wu[q][v], w1);
           VecB<E>::unpack(wg[q][v], w3);
 #pragma unroll
-          for (int i = 0; i < kN; ++i) dxf[v][i] = fmaf(dg, w3[i], fmaf(du, w1[i], dxf[v][i]));
+          for (int i = 0; i < kN; ++i) dxf[v][i] = fmaf(cf[q].x, w3[i], fmaf(cf[q].y, w1[i], dxf[v][i]));
         }
-        if (q < nq && lane == 0)
-          p.recs[pp[q]] = make_float4(__int_as_float(static_cast<int>(t)), dg, du, h);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -401,100 +457,98 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_token_kernel(BwdArgs
   }
 }
 
-// ---------------------------------------------------------------- token pass, lockstep (light rows)
-// 16 waves, one light row each; x[t] and dy[t] sit in LDS, the fp32 dx row in
-// VGPRs.  Every chunk of tiles starts with a workgroup barrier, so all
-// resident workgroups sweep the neurons in roughly the same order and the
-// weight rows (three per active pair) are reused from L2.  The two dot
-// products per pair use packed bf16 pairs (row_dot), so the rounding of u and
-// dh differs in the last bits from bwd_token_kernel's unpacked fp32 sums.
-constexpr int kSyncWavesB = 16;
-constexpr int kSyncListB = 96;  // {j, a, pos} entries per wave per chunk
+// Light rows in lockstep: 16 waves of TPW rows each, fp32 dx rows in VGPRs.
+// Every chunk of tiles starts with a workgroup barrier, so the resident
+// workgroups sweep the neurons in roughly the same order and the two weight
+// rows of each pair are reused from L2; each XCD's workgroups (dealt
+// round-robin) start at a different chunk and wrap around.
+constexpr int kDxWaves = 16;
+constexpr int kDxList = 128;      // {j, slot, row} entries per wave per chunk
+constexpr int kDxChunkMax = 4;    // 4 tiles x 128 neurons x 2 rows x 4 KB = 4 MB, an XCD's L2
 
-template <int NV>
-constexpr size_t bwd_sync_lds_bytes() {
-  return static_cast<size_t>(kSyncWavesB) * 2 * NV * kWave * 16 + kSyncWavesB * kSyncListB * 16;
-}
+constexpr size_t bwd_dx_sync_lds_bytes() { return static_cast<size_t>(kDxWaves) * kDxList * 16; }
 
-template <class E, int NV, int kC>
-__global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(BwdArgs p) {
+template <class E, int NV, int TPW, int kC>
+__global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
-  constexpr int kRowVec = NV * kWave;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  u32x4_t* xw = reinterpret_cast<u32x4_t*>(smem) + wave * kRowVec;
-  u32x4_t* yw = reinterpret_cast<u32x4_t*>(smem) + (kSyncWavesB + wave) * kRowVec;
-  int4* list = reinterpret_cast<int4*>(smem + kSyncWavesB * 2 * kRowVec * 16) + wave * kSyncListB;
+  int4* list = reinterpret_cast<int4*>(smem) + wave * kDxList;
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
-  const int64_t i_row = static_cast<int64_t>(blockIdx.x) * kSyncWavesB + wave;
-  const bool act = i_row < static_cast<int64_t>(p.split_n[0]);  // idle waves still meet every barrier
-  // wave-uniform: the token row stays in scalar registers
-  const int64_t t = act ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.light_rows[i_row])) : 0;
-  float dxf[NV][kN];
-  {
-    const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
-    const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
+  const int64_t n_rows = p.split_n[0];
+  int64_t tk[TPW];
+  bool act[TPW];
+  float dxf[TPW][NV][kN];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      // x, dy, the counts / indices and dx are touched once: non-temporal
-      // accesses keep them from pushing the shared weight rows out of L2
-      xw[v * kWave + lane] = act ? __builtin_nontemporal_load(xr + v * kWave + lane) : u32x4_t{0, 0, 0, 0};
-      yw[v * kWave + lane] = act ? __builtin_nontemporal_load(yr + v * kWave + lane) : u32x4_t{0, 0, 0, 0};
+  for (int k = 0; k < TPW; ++k) {
+    const int64_t i_row = (static_cast<int64_t>(blockIdx.x) * kDxWaves + wave) * TPW + k;
+    act[k] = i_row < n_rows;  // idle rows: the wave still takes part in the barriers
+    tk[k] = act[k] ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.light_rows[i_row])) : 0;
 #pragma unroll
-      for (int i = 0; i < kN; ++i) dxf[v][i] = 0.f;
-    }
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int i = 0; i < kN; ++i) dxf[k][v][i] = 0.f;
   }
-  const int chunk_tiles = max(1, min(kWave, kSyncListB / C));
-  // C = 16: the builder lanes load the next chunk's counts and 16 index bytes
-  // while the current chunk's entries are processed; an entry carries its
-  // slot position, from which its value and record position are loaded beside
-  // the weight rows.
+  // list builder lanes: lane = tile_in_chunk * TPW + row
+  const int chunk_tiles = max(1, min(min(kWave / TPW, kDxList / (C * TPW)), kDxChunkMax));
+  const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
+  const int rot = static_cast<int>(blockIdx.x & 7) * (n_chunks / 8);
+  const int kl = lane % TPW;
+  int my_tok = 0;  // token rows are < 2^31
+  bool my_act = false;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k)
+    if (kl == k) {
+      my_tok = static_cast<int>(tk[k]);
+      my_act = act[k] && lane < chunk_tiles * TPW;
+    }
+  // C = 16: the builder lane's count and 16 index bytes of the next chunk are
+  // loaded while the current chunk's entries are processed.
   int pf_cnt = 0;
   u32x4_t pf_idx{0, 0, 0, 0};
-  auto prefetch = [&](int b0) {
-    const int b = b0 + lane;
+  auto prefetch = [&](int c) {
+    const int b = ((c + rot) % n_chunks) * chunk_tiles + lane / TPW;
     pf_cnt = 0;
-    if (act && lane < chunk_tiles && b < n_t) {
-      const int64_t rec = t * n_t + b;
+    if (my_act && b < n_t) {
+      const int64_t rec = static_cast<int64_t>(my_tok) * n_t + b;
       pf_cnt = __builtin_nontemporal_load(p.count + rec);
       pf_idx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.idx + rec * 16));
     }
   };
   if constexpr (kC == 16) prefetch(0);
-  for (int b0 = 0; b0 < n_t; b0 += chunk_tiles) {
+  for (int c = 0; c < n_chunks; ++c) {
+    const int b0 = ((c + rot) % n_chunks) * chunk_tiles;
     __syncthreads();
-    const int b = b0 + lane;
+    const int b = b0 + lane / TPW;
     int total;
     if constexpr (kC == 16) {
       const int cnt = max(0, min(pf_cnt, 16));
       const u32x4_t ix = pf_idx;
+      const int spos = (my_tok * n_t + b) * 16;
       const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kSyncListB);
+      total = min(__shfl(incl, 63), kDxList);
       const int off = incl - cnt;
-      const int spos = static_cast<int>((t * n_t + b) * 16);
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) {
-        if (s2 < cnt && off + s2 < kSyncListB) {
+        if (s2 < cnt && off + s2 < kDxList) {
           const int j = b * tile_n + (static_cast<int>((ix[s2 >> 2] >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
-          list[off + s2] = make_int4(j, spos + s2, 0, 0);
+          list[off + s2] = make_int4(j, spos + s2, kl, 0);
         }
       }
-      if (b0 + chunk_tiles < n_t) prefetch(b0 + chunk_tiles);
+      if (c + 1 < n_chunks) prefetch(c + 1);
     } else {
       int cnt = 0;
-      if (act && lane < chunk_tiles && b < n_t) cnt = max(0, min(p.count[t * n_t + b], C));
+      if (my_act && b < n_t) cnt = max(0, min(p.count[static_cast<int64_t>(my_tok) * n_t + b], C));
       const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kSyncListB);
+      total = min(__shfl(incl, 63), kDxList);
       const int off = incl - cnt;
       if (cnt > 0) {
-        const int64_t rec = (t * n_t + b) * C;
-        // off + cnt <= chunk_tiles * C <= kSyncListB
-        for (int s2 = 0; s2 < cnt && off + s2 < kSyncListB; ++s2) {
-          const int j = b * tile_n + (p.idx[rec + s2] & (tile_n - 1));
-          list[off + s2] = make_int4(j, __float_as_int(load_elem<E>(p.val, rec + s2)), p.pos[rec + s2], 0);
-        }
+        const int rec = (my_tok * n_t + b) * C;
+        // off + cnt <= chunk_tiles * TPW * C <= kDxList by the launch's choice of TPW
+        for (int s2 = 0; s2 < cnt && off + s2 < kDxList; ++s2)
+          list[off + s2] = make_int4(b * tile_n + (p.idx[rec + s2] & (tile_n - 1)), rec + s2, kl, 0);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -503,83 +557,66 @@ __global__ __launch_bounds__(kSyncWavesB * kWave) void bwd_token_sync_kernel(Bwd
     for (int e = 0; e < total; ++e) {
       const int4 ent = list[e];
       const int j = __builtin_amdgcn_readfirstlane(ent.x);
-      float a;
-      int pp;
-      if constexpr (kC == 16) {
-        const int sp = __builtin_amdgcn_readfirstlane(ent.y);
-        a = load_elem<E>(p.val, sp);
-        pp = p.pos[sp];
-      } else {
-        a = __int_as_float(__builtin_amdgcn_readfirstlane(ent.y));
-        pp = __builtin_amdgcn_readfirstlane(ent.z);
-      }
+      const float2 cf = p.coef[__builtin_amdgcn_readfirstlane(ent.y)];
+      const int kk = __builtin_amdgcn_readfirstlane(ent.z);
       const int64_t ro = int64_t(j) * d * E::kBytes;
-      const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
-      const u32x4_t* dr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_down) + ro);
       const u32x4_t* gr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_gate_t) + ro);
-      u32x4_t wu[NV], wd[NV], wg[NV];
+      const u32x4_t* ur = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.w_up_t) + ro);
+      u32x4_t wg[NV], wu[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        wu[v] = ur[v * kWave + lane];
-        wd[v] = dr[v * kWave + lane];
         wg[v] = gr[v * kWave + lane];
-      }
-      // x and dy come from LDS one 16-byte piece at a time (fewer live VGPRs)
-      float au[4] = {0.f, 0.f, 0.f, 0.f}, ae[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const u32x4_t xv = xw[v * kWave + lane];
-        row_dot_piece<E>(wu[v], xv, au);
-        __builtin_amdgcn_sched_barrier(0);
+        wu[v] = ur[v * kWave + lane];
       }
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const u32x4_t yv = yw[v * kWave + lane];
-        row_dot_piece<E>(wd[v], yv, ae);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const float pu = (au[0] + au[1]) + (au[2] + au[3]);
-      const float pe = (ae[0] + ae[1]) + (ae[2] + ae[3]);
-      const float u = wave_sum(pu), ee = wave_sum(pe);
-      const float h = a * u;
-      const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-      const float dh = ee + p.l1 * sg;
-      const float du = dh * a;
-      const float dg = dh * u;
+      for (int k = 0; k < TPW; ++k) {
+        if (kk == k) {  // wave-uniform
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float w1[kN], w3[kN];
-        VecB<E>::unpack(wu[v], w1);
-        VecB<E>::unpack(wg[v], w3);
+          for (int v = 0; v < NV; ++v) {
+            float w1[kN], w3[kN];
+            VecB<E>::unpack(wu[v], w1);
+            VecB<E>::unpack(wg[v], w3);
 #pragma unroll
-        for (int i = 0; i < kN; ++i) dxf[v][i] = fmaf(dg, w3[i], fmaf(du, w1[i], dxf[v][i]));
+            for (int i = 0; i < kN; ++i) dxf[k][v][i] = fmaf(cf.x, w3[i], fmaf(cf.y, w1[i], dxf[k][v][i]));
+          }
+        }
       }
-      if (lane == 0) p.recs[pp] = make_float4(__int_as_float(static_cast<int>(t)), dg, du, h);
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if (act) {
-    u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + t * d * E::kBytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(VecB<E>::pack(dxf[v]), dxr + v * kWave + lane);
+  for (int k = 0; k < TPW; ++k) {
+    if (act[k]) {
+      u32x4_t* dxr = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dx) + tk[k] * d * E::kBytes);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(VecB<E>::pack(dxf[k][v]), dxr + v * kWave + lane);
+    }
   }
 }
 
-template <class E, int NV, int kC>
-static hipError_t launch_bwd_sync_c(const BwdArgs& a, hipStream_t s) {
-  constexpr size_t lds = bwd_sync_lds_bytes<NV>();
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_token_sync_kernel<E, NV, kC>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+template <class E, int NV, int TPW, int kC>
+static hipError_t launch_bwd_dx_sync_c(const BwdArgs& a, hipStream_t s) {
+  constexpr size_t lds = bwd_dx_sync_lds_bytes();
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((bwd_token_sync_kernel<E, NV, kC>), dim3(static_cast<unsigned>((a.T + kSyncWavesB - 1) / kSyncWavesB)),
-                     dim3(kSyncWavesB * kWave), lds, s, a);
+  constexpr int64_t per_block = static_cast<int64_t>(kDxWaves) * TPW;
+  hipLaunchKernelGGL((bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
+                     dim3(static_cast<unsigned>((a.T + per_block - 1) / per_block)), dim3(kDxWaves * kWave), lds, s,
+                     a);
   return hipGetLastError();
 }
+// Rows per wave: two fp32 dx rows beside one pair's two weight rows fit the
+// 128 VGPRs of a 16-wave workgroup up to d_model = 2048 (bf16) / 1024 (fp32);
+// TPW * C <= kDxList, so every chunk of >= 1 tile fits the list.
 template <class E, int NV>
-static hipError_t launch_bwd_sync(const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_dx_sync(const BwdArgs& a, hipStream_t s) {
+  constexpr bool two = NV * VecB<E>::N <= 32;
   if constexpr (E::kBytes == 2)
-    if (a.C == 16) return launch_bwd_sync_c<E, NV, 16>(a, s);
-  return launch_bwd_sync_c<E, NV, 0>(a, s);
+    if (a.C == 16) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 16>(a, s);
+  if (two && 2 * a.C <= kDxList) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 0>(a, s);
+  return launch_bwd_dx_sync_c<E, NV, 1, 0>(a, s);
 }
 
 // ---------------------------------------------------------------- row totals (for the split)
@@ -602,69 +639,6 @@ __global__ __launch_bounds__(256) void bwd_totals_kernel(BwdArgs p) {
   }
 }
 
-// ---------------------------------------------------------------- per-neuron weight gradients
-template <class E, int NV>
-__global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
-  constexpr int kN = VecB<E>::N;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  if (j >= p.F) return;
-  const int d = p.d;
-  float ag[NV][kN], au[NV][kN], ad[NV][kN];
-#pragma unroll
-  for (int v = 0; v < NV; ++v)
-#pragma unroll
-    for (int i = 0; i < kN; ++i) ag[v][i] = au[v][i] = ad[v][i] = 0.f;
-  const int beg = p.neuron_off[j], end = p.neuron_off[j + 1];
-  constexpr int kP = 2;
-  for (int e0 = beg; e0 < end; e0 += kP) {
-    float4 rr[kP];
-    u32x4_t xv[kP][NV], yv[kP][NV];
-#pragma unroll
-    for (int q = 0; q < kP; ++q) {
-      const bool live = e0 + q < end;
-      rr[q] = live ? p.recs[e0 + q] : make_float4(0.f, 0.f, 0.f, 0.f);
-      // clamped so that a corrupted record cannot address outside x / dy
-      const int64_t t = min(max(static_cast<int64_t>(__float_as_int(rr[q].x)), int64_t(0)), p.T - 1);
-      const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
-      const u32x4_t* yr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.dy) + t * d * E::kBytes);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        xv[q][v] = live ? xr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
-        yv[q][v] = live ? yr[v * kWave + lane] : u32x4_t{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kP; ++q) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        float xf[kN], yf[kN];
-        VecB<E>::unpack(xv[q][v], xf);
-        VecB<E>::unpack(yv[q][v], yf);
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          ag[v][i] = fmaf(rr[q].y, xf[i], ag[v][i]);
-          au[v][i] = fmaf(rr[q].z, xf[i], au[v][i]);
-          ad[v][i] = fmaf(rr[q].w, yf[i], ad[v][i]);
-        }
-      }
-    }
-  }
-  float* og = p.dw_gate_t + j * d;
-  float* ou = p.dw_up_t + j * d;
-  float* od = p.dw_down + j * d;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int64_t c = static_cast<int64_t>(v * kWave + lane) * kN;
-#pragma unroll
-    for (int i = 0; i < kN; i += 4) {
-      *reinterpret_cast<f32x4_t*>(og + c + i) = f32x4_t{ag[v][i], ag[v][i + 1], ag[v][i + 2], ag[v][i + 3]};
-      *reinterpret_cast<f32x4_t*>(ou + c + i) = f32x4_t{au[v][i], au[v][i + 1], au[v][i + 2], au[v][i + 3]};
-      *reinterpret_cast<f32x4_t*>(od + c + i) = f32x4_t{ad[v][i], ad[v][i + 1], ad[v][i + 2], ad[v][i + 3]};
-    }
-  }
-}
-
 // ---------------------------------------------------------------- launch
 template <class E, int NV>
 static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
@@ -683,44 +657,48 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
   if (nblk) {
     hipLaunchKernelGGL(bwd_pos_kernel, dim3(nblk, nchunk), dim3(64), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (NV <= 4) {
-      // light rows in lockstep, heavy rows cut into tile ranges
-      const unsigned tblk = static_cast<unsigned>((a.T + 255) / 256);
-      hipLaunchKernelGGL(bwd_totals_kernel, dim3(tblk), dim3(256), 0, s, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      RouteArgs r{};
-      r.T = a.T;
-      r.C = a.C;
-      r.ell_rows = const_cast<int32_t*>(a.ell_rows);
-      r.n_rows = const_cast<int32_t*>(a.n_rows);
-      r.row_total = a.row_total;
-      r.block_total = a.block_total;
-      r.light_rows = a.light_rows;
-      r.heavy_rows = a.heavy_rows;
-      r.split_n = a.split_n;
-      r.block_heavy = a.block_heavy;
-      r.heavy_cap = a.heavy_cap;
-      if ((e = launch_route_split(r, s)) != hipSuccess) return e;
-      if ((e = launch_bwd_sync<E, NV>(a, s)) != hipSuccess) return e;
-      const int64_t units = a.heavy_cap * a.groups;
-      if (units > 0) {
-        hipLaunchKernelGGL((bwd_token_kernel<E, NV, true>),
-                           dim3(static_cast<unsigned>((units + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave),
-                           0, s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        e = launch_splitk_reduce(a.dx_hpart, a.groups, a.heavy_cap, a.split_n + 1, a.heavy_rows, a.dx, a.d,
-                                 E::kBytes == 2 ? 1 : 0, s);
-        if (e != hipSuccess) return e;
-      }
-    } else {
-      hipLaunchKernelGGL((bwd_token_kernel<E, NV, false>),
-                         dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0,
+  }
+  // per-neuron pass: the weight gradients (zero rows when T == 0) and the
+  // (dg, du) of every stored slot, which the dx pass reads
+  hipLaunchKernelGGL((bwd_dw_kernel<E, NV>), dim3(static_cast<unsigned>((a.F + 3) / 4)), dim3(4 * kWave), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!nblk) return hipSuccess;
+  if constexpr (NV <= 4) {
+    // light rows in lockstep, heavy rows cut into tile ranges
+    const unsigned tblk = static_cast<unsigned>((a.T + 255) / 256);
+    hipLaunchKernelGGL(bwd_totals_kernel, dim3(tblk), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    RouteArgs r{};
+    r.T = a.T;
+    r.C = a.C;
+    r.ell_rows = const_cast<int32_t*>(a.ell_rows);
+    r.n_rows = const_cast<int32_t*>(a.n_rows);
+    r.row_total = a.row_total;
+    r.block_total = a.block_total;
+    r.light_rows = a.light_rows;
+    r.heavy_rows = a.heavy_rows;
+    r.split_n = a.split_n;
+    r.block_heavy = a.block_heavy;
+    r.heavy_cap = a.heavy_cap;
+    if ((e = launch_route_split(r, s)) != hipSuccess) return e;
+    if ((e = launch_bwd_dx_sync<E, NV>(a, s)) != hipSuccess) return e;
+    const int64_t units = a.heavy_cap * a.groups;
+    if (units > 0) {
+      hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, true>),
+                         dim3(static_cast<unsigned>((units + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0,
                          s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      e = launch_splitk_reduce(a.dx_hpart, a.groups, a.heavy_cap, a.split_n + 1, a.heavy_rows, a.dx, a.d,
+                               E::kBytes == 2 ? 1 : 0, s);
+      if (e != hipSuccess) return e;
     }
+  } else {
+    hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, false>),
+                       dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0, s,
+                       a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dw_kernel<E, NV>), dim3(static_cast<unsigned>((a.F + 3) / 4)), dim3(4 * kWave), 0, s, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <class E>

@@ -90,6 +90,14 @@ def test_backward_fp32():
     run_bwd(w, 256, label="fp32 C=2")
 
 
+def test_backward_wide_rows():
+    """d_model = 4096 (bf16), the widest rows the library takes: the dx pass
+    then runs one wave per ELL row instead of the lockstep workgroups."""
+    import dataclasses
+    w = dataclasses.replace(W.workload(4, T=160), d_model=4096)
+    run_bwd(w, 64, label="d_model=4096")
+
+
 def test_backward_deterministic():
     w = W.workload(4, T=900)
     a = run_bwd(w, 512, label="det a", check=False)
