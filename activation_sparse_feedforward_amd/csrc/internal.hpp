@@ -132,11 +132,13 @@ struct BwdArgs {
   float* dw_down;
   // workspace
   int32_t* blk_hist;    // [ceil(T/64)][F]
+  unsigned long long* blk_mask;  // [ceil(T/64)][F] rows of each 64-row block holding each neuron
   int32_t* neuron_off;  // [F + 1]
   int2* pairs;          // [T * n_t * C] neuron-major {t, slot}
   float2* coef;         // [T][n_t][C] (dg, du) of each stored slot
   float* g_d;           // [cap][F]
   float* u_d;           // [cap][F]
+  float* e_d;           // [cap][F] dy_d W_down^T
   void* dg_d;           // [cap][F] dtype
   void* du_d;
   void* h_d;

@@ -14,12 +14,14 @@
 //                                                            (neuron-major)
 // TwELL is token-major, so the pairs are transposed to neuron-major order by a
 // counting sort that keeps ascending t inside each neuron (deterministic dW):
-//   hist     per block of 64 ELL rows, LDS histogram of neuron ids
-//   colscan  per neuron, exclusive scan over the blocks
+//   mask     per block of 64 ELL rows and neuron, the 64-bit mask of the rows
+//            holding it (within one row every neuron occurs at most once) and
+//            its popcount
+//   colscan  per neuron, exclusive scan of the counts over the blocks
 //   nscan    exclusive scan over neurons -> start of each neuron's pair list
-//   pos      per block, rows in order, one LDS cursor per neuron -> the pair
-//            list {t, slot} in neuron-major order (within one row every
-//            neuron occurs at most once, so a wave's lanes never collide)
+//   pos      per (row, tile), independent: a pair's place in its neuron's list
+//            from the scans and a popcount of the mask below its row -> the
+//            pair list {t, slot} in neuron-major order
 //   dw       one wave per neuron j: W_up^T[j] and W_down[j] stay in VGPRs
 //            while the wave walks j's pairs in ascending t, gathering x[t] and
 //            dy[t]; it forms u, dh, dg, du, h for each pair, stores (dg, du)
@@ -45,7 +47,7 @@ namespace twell {
 namespace {
 
 constexpr int kBlkRows = 64;         // ELL rows per counting-sort block
-constexpr int kNeuronChunk = 8192;   // neurons per LDS histogram / cursor table
+constexpr int kNeuronChunk = 8192;   // neurons per LDS mask table (64 KB)
 constexpr int kTokWaves = 4;
 constexpr int kTokListCap = 512;
 
@@ -135,13 +137,16 @@ __device__ __forceinline__ float row_dot(const u32x4_t* w, const u32x4_t* x) {
 
 }  // namespace
 
-// ---------------------------------------------------------------- hist
-__global__ __launch_bounds__(256) void bwd_hist_kernel(BwdArgs p) {
-  __shared__ int hist[kNeuronChunk];
+// ---------------------------------------------------------------- row masks
+// Per block of 64 ELL rows and neuron j: a 64-bit mask of the block's rows
+// whose stored slots hold j (bit r = row 64 blk + r); its popcount is the
+// block's count for j.
+__global__ __launch_bounds__(256) void bwd_mask_kernel(BwdArgs p) {
+  __shared__ unsigned long long mask[kNeuronChunk];
   const int blk = blockIdx.x;
   const int j0 = blockIdx.y * kNeuronChunk;
   const int nj = min(kNeuronChunk, p.F - j0);
-  for (int j = threadIdx.x; j < nj; j += 256) hist[j] = 0;
+  for (int j = threadIdx.x; j < nj; j += 256) mask[j] = 0ull;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_t = p.F / p.tile_n;
@@ -155,27 +160,45 @@ __global__ __launch_bounds__(256) void bwd_hist_kernel(BwdArgs p) {
       const int64_t rec = (t * n_t + b) * p.C;
       for (int s = 0; s < cnt; ++s) {
         const int j = b * p.tile_n + (p.idx[rec + s] & (p.tile_n - 1)) - j0;
-        if (j >= 0 && j < nj) atomicAdd(&hist[j], 1);
+        if (j >= 0 && j < nj) atomicOr(&mask[j], 1ull << r);
       }
     }
   }
   __syncthreads();
-  int32_t* out = p.blk_hist + static_cast<int64_t>(blk) * p.F + j0;
-  for (int j = threadIdx.x; j < nj; j += 256) out[j] = hist[j];
+  const int64_t o = static_cast<int64_t>(blk) * p.F + j0;
+  for (int j = threadIdx.x; j < nj; j += 256) {
+    const unsigned long long m = mask[j];
+    p.blk_mask[o + j] = m;
+    p.blk_hist[o + j] = __popcll(m);
+  }
 }
 
 // ---------------------------------------------------------------- column scan
+// Per neuron, exclusive scan of the block counts over the blocks (in place);
+// the total goes to neuron_off[j].  A workgroup takes 32 neurons, each in 8
+// segments of blocks summed in parallel.
 __global__ __launch_bounds__(256) void bwd_colscan_kernel(BwdArgs p, int nblk) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= p.F) return;
+  __shared__ int seg_sum[8][32];
+  const int jl = threadIdx.x & 31, seg = threadIdx.x >> 5;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 32 + jl;
+  const int per = (nblk + 7) / 8;
+  const int b0 = min(nblk, seg * per), b1 = min(nblk, b0 + per);
+  int32_t* h = p.blk_hist + j;
+  int sum = 0;
+  if (j < p.F)
+    for (int b = b0; b < b1; ++b) sum += h[static_cast<int64_t>(b) * p.F];
+  seg_sum[seg][jl] = sum;
+  __syncthreads();
   int run = 0;
-  for (int b = 0; b < nblk; ++b) {
-    int32_t* h = p.blk_hist + static_cast<int64_t>(b) * p.F + j;
-    const int c = *h;
-    *h = run;
-    run += c;
+  for (int k = 0; k < seg; ++k) run += seg_sum[k][jl];
+  if (j < p.F) {
+    for (int b = b0; b < b1; ++b) {
+      const int c = h[static_cast<int64_t>(b) * p.F];
+      h[static_cast<int64_t>(b) * p.F] = run;
+      run += c;
+    }
+    if (seg == 7) p.neuron_off[j] = run;  // per-neuron total; turned into offsets by nscan
   }
-  p.neuron_off[j] = run;  // per-neuron total; turned into offsets by nscan
 }
 
 // ---------------------------------------------------------------- neuron scan (one block)
@@ -201,43 +224,29 @@ __global__ __launch_bounds__(1024) void bwd_nscan_kernel(BwdArgs p) {
   if (threadIdx.x == 0) p.neuron_off[p.F] = carry_s;
 }
 
-// ---------------------------------------------------------------- positions (one wave per block)
-__global__ __launch_bounds__(64) void bwd_pos_kernel(BwdArgs p) {
-  __shared__ int cursor[kNeuronChunk];
-  const int blk = blockIdx.x;
-  const int j0 = blockIdx.y * kNeuronChunk;
-  const int nj = min(kNeuronChunk, p.F - j0);
-  const int lane = threadIdx.x;
-  const int32_t* hb = p.blk_hist + static_cast<int64_t>(blk) * p.F + j0;
-  for (int j = lane; j < nj; j += 64) cursor[j] = p.neuron_off[j0 + j] + hb[j];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// ---------------------------------------------------------------- positions
+// One thread per (ELL row i, tile): the pair (i, j) goes to
+//   neuron_off[j] + (pairs of j in earlier blocks) + (rows of i's block
+//   before i that hold j),
+// the last term a popcount of the block's row mask below bit i % 64, so each
+// neuron's pairs come out in ascending i (= ascending t) with no ordering
+// between threads.
+__global__ __launch_bounds__(256) void bwd_pos_kernel(BwdArgs p) {
   const int n_t = p.F / p.tile_n;
-  const int64_t n_ell = n_ell_of(p);
-  for (int r = 0; r < kBlkRows; ++r) {
-    const int64_t i = static_cast<int64_t>(blk) * kBlkRows + r;
-    if (i >= n_ell) break;
-    const int64_t t = p.ell_rows[i];
-    for (int b0 = 0; b0 < n_t; b0 += 64) {
-      const int b = b0 + lane;
-      const int cnt = b < n_t ? max(0, min(p.count[t * n_t + b], p.C)) : 0;
-      const int maxc = wave_max(cnt);
-      const int64_t rec = (t * n_t + b) * p.C;
-      for (int s = 0; s < maxc; ++s) {
-        if (s < cnt) {
-          const int j = b * p.tile_n + (p.idx[rec + s] & (p.tile_n - 1)) - j0;
-          if (j >= 0 && j < nj) {
-            const int q = cursor[j];
-            cursor[j] = q + 1;
-            p.pairs[q] = make_int2(static_cast<int>(t), static_cast<int>(rec + s));
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-    }
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t i = u / n_t;
+  const int b = static_cast<int>(u - i * n_t);
+  if (i >= n_ell_of(p)) return;
+  const int64_t t = p.ell_rows[i];
+  const int cnt = max(0, min(p.count[t * n_t + b], p.C));
+  const int r = static_cast<int>(i & (kBlkRows - 1));
+  const unsigned long long below = (1ull << r) - 1ull;
+  const int64_t blk_off = (i / kBlkRows) * p.F;
+  const int64_t rec = (t * n_t + b) * p.C;
+  for (int s = 0; s < cnt; ++s) {
+    const int j = b * p.tile_n + (p.idx[rec + s] & (p.tile_n - 1));
+    const int q = p.neuron_off[j] + p.blk_hist[blk_off + j] + __popcll(p.blk_mask[blk_off + j] & below);
+    p.pairs[q] = make_int2(static_cast<int>(t), static_cast<int>(rec + s));
   }
 }
 
@@ -647,15 +656,16 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
   const unsigned nchunk = static_cast<unsigned>((a.F + kNeuronChunk - 1) / kNeuronChunk);
   hipError_t e;
   if (nblk) {
-    hipLaunchKernelGGL(bwd_hist_kernel, dim3(nblk, nchunk), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_mask_kernel, dim3(nblk, nchunk), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_colscan_kernel, dim3((a.F + 255) / 256), dim3(256), 0, s, a, static_cast<int>(nblk));
+  hipLaunchKernelGGL(bwd_colscan_kernel, dim3((a.F + 31) / 32), dim3(256), 0, s, a, static_cast<int>(nblk));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_nscan_kernel, dim3(1), dim3(1024), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (nblk) {
-    hipLaunchKernelGGL(bwd_pos_kernel, dim3(nblk, nchunk), dim3(64), 0, s, a);
+    const int64_t units = a.T * (a.F / a.tile_n);  // (row, tile) pairs; rows past n_ell exit
+    hipLaunchKernelGGL(bwd_pos_kernel, dim3(static_cast<unsigned>((units + 255) / 256)), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // per-neuron pass: the weight gradients (zero rows when T == 0) and the

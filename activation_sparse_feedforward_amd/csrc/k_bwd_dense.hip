@@ -1,16 +1,20 @@
 // Backward of the rows the hybrid format sent to the dense fallback, on MFMA.
 //
 // Same loss as the sparse backward (sum(y*dy) + l1 sum|h|, h = ReLU(g)*u); for
-// these few rows everything is dense, so it is four GEMM launches over the
+// these few rows everything is dense, so it is GEMM launches over the
 // gathered rows (n_dense is read on the device; workgroups past it exit):
-//   gu:  g, u = x_d W_gate, x_d W_up (recomputed, fp32 into the workspace)
-//   dh:  dh = dy_d W_down^T, epilogue: + l1 sign(h); du = dh a; dg = dh u [g>0]
+//   gue: g, u, e = x_d W_gate, x_d W_up, dy_d W_down^T (recomputed; one launch,
+//        blockIdx.z picks the product; fp32 into the workspace)
+//   act: elementwise dh = e + l1 sign(h), du = dh a, dg = dh u [g>0]
 //        -> dG, dU, H (dtype) in the workspace
 //   dx:  dx_d = dG W_gate^T... in the stored layout: dx[t,k] = sum_j dG[m,j] W_gate^T[j,k]
 //        + dU[m,j] W_up^T[j,k]; two K passes into one accumulator, rows scattered
 //   dw:  dW_gate^T += dG^T x_d, dW_up^T += dU^T x_d, dW_down += H^T dy_d
 //        (both operands MN-contiguous, K = n_dense, fp32 read-modify-write on
 //        top of the sparse rows' contribution written before)
+// The dense rows are few (n_dense ~ 250 of 16384 at the training workload), so
+// the three products share one launch of 3 x d_ff/128 workgroups instead of
+// leaving most of the chip idle in two smaller ones.
 #include "gemm_core.hpp"
 #include "internal.hpp"
 
@@ -18,56 +22,38 @@ namespace twell {
 
 namespace {
 __device__ __forceinline__ int64_t n_dense_of(const BwdArgs& p) { return static_cast<int64_t>(p.n_rows[1]); }
+
+// K slices [0, nk) from base b0, [nk, 2 nk) from base b1, through one loader.
+template <class L>
+struct TwoSource {
+  L& l;
+  const char* b0;
+  const char* b1;
+  int nk;
+  __device__ __forceinline__ void load(int kt) {
+    l.base = kt < nk ? b0 : b1;
+    l.load(kt < nk ? kt : kt - nk);
+  }
+  __device__ __forceinline__ void store(char* lds, int row_base) const { l.store(lds, row_base); }
+};
 }  // namespace
 
+// blockIdx.z: 0 -> g = x_d W_gate, 1 -> u = x_d W_up, 2 -> e = dy_d W_down^T
 template <class E>
-__global__ __launch_bounds__(kThreads, 2) void bwd_gu_kernel(BwdArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_gue_kernel(BwdArgs p) {
   extern __shared__ __align__(16) char lds[];
   const int64_t n = n_dense_of(p);
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   if (m0 >= n) return;
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
-  KRowLoader<E, kBM> la;
-  la.init(p.x, p.d, m0, n, p.dense_rows);
-  struct {
-    KRowLoader<E, 64> g, u;
-    __device__ void load(int kt) { g.load(kt); u.load(kt); }
-    __device__ void store(char* l, int) const { g.store(l, 0); u.store(l, 64); }
-  } lb;
-  lb.g.init(p.w_gate_t, p.d, j0, p.F, nullptr);
-  lb.u.init(p.w_up_t, p.d, j0, p.F, nullptr);
-  Acc<128> acc;
-  gemm_mainloop<E, 128>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
-  const int lane = threadIdx.x & 63;
-  const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t m = wrow0 + mb * 32 + acc_row(r, lane);
-      if (m >= n) continue;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int64_t o = m * p.F + j0 + nb * 32 + (lane & 31);
-        p.g_d[o] = acc.c[mb][nb][r];
-        p.u_d[o] = acc.c[mb][nb + 2][r];
-      }
-    }
-}
-
-template <class E>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dh_kernel(BwdArgs p) {
-  extern __shared__ __align__(16) char lds[];
-  const int64_t n = n_dense_of(p);
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  if (m0 >= n) return;
+  const int z = blockIdx.z;
   const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 128;
   KRowLoader<E, kBM> la;
-  la.init(p.dy, p.d, m0, n, p.dense_rows);
+  la.init(z == 2 ? p.dy : p.x, p.d, m0, n, p.dense_rows);
   KRowLoader<E, 128> lb;
-  lb.init(p.w_down, p.d, j0, p.F, nullptr);
+  lb.init(z == 0 ? p.w_gate_t : (z == 1 ? p.w_up_t : p.w_down), p.d, j0, p.F, nullptr);
   Acc<128> acc;
   gemm_mainloop<E, 128>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
+  float* out = z == 0 ? p.g_d : (z == 1 ? p.u_d : p.e_d);
   const int lane = threadIdx.x & 63;
   const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
 #pragma unroll
@@ -79,18 +65,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dh_kernel(BwdArgs p) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         const int64_t j = j0 + nb * 32 + (lane & 31);
-        if (j >= p.F) continue;  // d_ff need only be a multiple of 64
-        const int64_t o = m * p.F + j;
-        const float g = p.g_d[o], u = p.u_d[o];
-        const float a = g > 0.f ? g : 0.f;
-        const float h = a * u;
-        const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
-        const float dh = acc.c[mb][nb][r] + p.l1 * sg;
-        store_bits<E>(p.du_d, o, round_store<E>(dh * a).bits);
-        store_bits<E>(p.dg_d, o, round_store<E>(g > 0.f ? dh * u : 0.f).bits);
-        store_bits<E>(p.h_d, o, round_store<E>(h).bits);
+        if (j < p.F) out[m * p.F + j] = acc.c[mb][nb][r];  // d_ff need only be a multiple of 64
       }
     }
+}
+
+// Four consecutive neurons of one dense row per thread.
+template <class E>
+__global__ __launch_bounds__(256) void bwd_dense_act_kernel(BwdArgs p) {
+  const int64_t n = n_dense_of(p);
+  const int64_t q = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (q >= n * p.F) return;  // F is a multiple of 64, so the 4 elements share a row
+  const float4 g4 = *reinterpret_cast<const float4*>(p.g_d + q);
+  const float4 u4 = *reinterpret_cast<const float4*>(p.u_d + q);
+  const float4 e4 = *reinterpret_cast<const float4*>(p.e_d + q);
+  const float gs[4] = {g4.x, g4.y, g4.z, g4.w}, us[4] = {u4.x, u4.y, u4.z, u4.w}, es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g = gs[i], u = us[i];
+    const float a = g > 0.f ? g : 0.f;
+    const float h = a * u;
+    const float sg = h > 0.f ? 1.f : (h < 0.f ? -1.f : 0.f);
+    const float dh = es[i] + p.l1 * sg;
+    store_bits<E>(p.du_d, q + i, round_store<E>(dh * a).bits);
+    store_bits<E>(p.dg_d, q + i, round_store<E>(g > 0.f ? dh * u : 0.f).bits);
+    store_bits<E>(p.h_d, q + i, round_store<E>(h).bits);
+  }
 }
 
 template <class E>
@@ -104,21 +104,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dx_kernel(BwdArgs p) {
   const int splits = p.dx_splits > 1 ? p.dx_splits : 1;
   const int64_t ks = p.F / splits, k0 = static_cast<int64_t>(blockIdx.z) * ks;
   const int nk = static_cast<int>(ks / KRowLoader<E, kBM>::kSliceElems);
+  // one main loop over 2 nk slices: (dG, W_gate^T) then (dU, W_up^T), the
+  // same loaders re-pointed (two inlined loops spilled the accumulators)
+  KRowLoader<E, kBM> la;
+  la.init(static_cast<const char*>(p.dg_d) + k0 * E::kBytes, p.F, m0, n, nullptr);
+  MNColLoader<E, 128> lb;
+  lb.init(static_cast<const char*>(p.w_gate_t) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
+  TwoSource<KRowLoader<E, kBM>> sa{la, la.base, static_cast<const char*>(p.du_d) + k0 * E::kBytes, nk};
+  TwoSource<MNColLoader<E, 128>> sb{lb, lb.base, static_cast<const char*>(p.w_up_t) + k0 * p.d * E::kBytes, nk};
   Acc<128> acc;
-  {
-    KRowLoader<E, kBM> la;
-    la.init(static_cast<const char*>(p.dg_d) + k0 * E::kBytes, p.F, m0, n, nullptr);
-    MNColLoader<E, 128> lb;
-    lb.init(static_cast<const char*>(p.w_gate_t) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
-    gemm_mainloop<E, 128>(la, lb, nk, lds, acc);
-  }
-  {
-    KRowLoader<E, kBM> la;
-    la.init(static_cast<const char*>(p.du_d) + k0 * E::kBytes, p.F, m0, n, nullptr);
-    MNColLoader<E, 128> lb;
-    lb.init(static_cast<const char*>(p.w_up_t) + k0 * p.d * E::kBytes, p.d, n0, p.d, ks);
-    gemm_mainloop<E, 128>(la, lb, nk, lds, acc, /*accumulate=*/true);
-  }
+  gemm_mainloop<E, 128>(sa, sb, 2 * nk, lds, acc);
   const int lane = threadIdx.x & 63;
   const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
 #pragma unroll
@@ -179,10 +174,11 @@ template <class E>
 static hipError_t launch_bwd_dense_t(const BwdArgs& a, hipStream_t s) {
   const unsigned mrows = static_cast<unsigned>((a.cap + kBM - 1) / kBM);
   const size_t lds = (kBM + 128) * 128;
-  hipLaunchKernelGGL((bwd_gu_kernel<E>), dim3(a.F / 64, mrows), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((bwd_gue_kernel<E>), dim3((a.F + 127) / 128, mrows, 3), dim3(kThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dh_kernel<E>), dim3((a.F + 127) / 128, mrows), dim3(kThreads), lds, s, a);
+  const int64_t quads = a.cap * a.F / 4;
+  hipLaunchKernelGGL((bwd_dense_act_kernel<E>), dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int splits = a.dx_splits > 1 ? a.dx_splits : 1;
   hipLaunchKernelGGL((bwd_dx_kernel<E>), dim3(a.d / 128, mrows, splits), dim3(kThreads), lds, s, a);

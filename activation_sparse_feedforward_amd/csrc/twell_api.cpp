@@ -93,7 +93,7 @@ HybridWs hybrid_ws(const twell_desc* d, int64_t max_dense_rows) {
 
 // Workspace layout of the backward.
 struct BwdWs {
-  size_t blk_hist, neuron_off, pairs, coef, g_d, u_d, dg_d, du_d, h_d, dx_part, row_total, block_total, block_heavy,
+  size_t blk_hist, blk_mask, neuron_off, pairs, coef, g_d, u_d, e_d, dg_d, du_d, h_d, dx_part, row_total, block_total, block_heavy,
       light, heavy, split_n, dx_hpart, total;
 };
 BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
@@ -103,11 +103,13 @@ BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
   const size_t cap = static_cast<size_t>(max_dense_rows), eb = static_cast<size_t>(elem_bytes(d));
   size_t o = 0;
   w.blk_hist = o;   o += align256(((T + 63) / 64) * F * 4);
+  w.blk_mask = o;   o += align256(((T + 63) / 64) * F * 8);
   w.neuron_off = o; o += align256((F + 1) * 4);
   w.pairs = o;      o += align256(slots * 8);
   w.coef = o;       o += align256(slots * 8);
   w.g_d = o;        o += align256(cap * F * 4);
   w.u_d = o;        o += align256(cap * F * 4);
+  w.e_d = o;        o += align256(cap * F * 4);
   w.dg_d = o;       o += align256(cap * F * eb);
   w.du_d = o;       o += align256(cap * F * eb);
   w.h_d = o;        o += align256(cap * F * eb);
@@ -348,11 +350,13 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.dw_up_t = dw_up_t;
   a.dw_down = dw_down;
   a.blk_hist = reinterpret_cast<int32_t*>(wsb + bw.blk_hist);
+  a.blk_mask = reinterpret_cast<unsigned long long*>(wsb + bw.blk_mask);
   a.neuron_off = reinterpret_cast<int32_t*>(wsb + bw.neuron_off);
   a.pairs = reinterpret_cast<int2*>(wsb + bw.pairs);
   a.coef = reinterpret_cast<float2*>(wsb + bw.coef);
   a.g_d = reinterpret_cast<float*>(wsb + bw.g_d);
   a.u_d = reinterpret_cast<float*>(wsb + bw.u_d);
+  a.e_d = reinterpret_cast<float*>(wsb + bw.e_d);
   a.dg_d = wsb + bw.dg_d;
   a.du_d = wsb + bw.du_d;
   a.h_d = wsb + bw.h_d;
