@@ -144,7 +144,7 @@ struct BwdArgs {
   void* h_d;
   float* dx_part;       // [dx_splits][cap][d] fp32 split-K partials of the dense rows' dx
   int32_t dx_splits;
-  // light / heavy split of the ELL rows for the token pass (as in the hybrid forward)
+  // light / heavy split of the ELL rows for the dx pass (as in the hybrid forward)
   int32_t* row_total;    // [T]
   int32_t* block_total;  // [ceil(T/256)]
   int32_t* light_rows;   // [T]
