@@ -98,6 +98,12 @@ def test_backward_wide_rows():
     run_bwd(w, 64, label="d_model=4096")
 
 
+def test_backward_wide_ff():
+    """d_ff = 16384: the pair transpose's per-block row masks span two
+    8192-neuron chunks."""
+    run_bwd(W.workload(4, T=200, d_model=512, d_ff=16384), 64, label="d_ff=16384")
+
+
 def test_backward_deterministic():
     w = W.workload(4, T=900)
     a = run_bwd(w, 512, label="det a", check=False)

@@ -101,10 +101,12 @@ CASES = [
     ("T=1", W.workload(2, T=1)),
     ("c4 lognormal tail", W.workload(4, T=520)),
     ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
+    ("wide d_ff=16384", W.workload(4, T=300, d_model=512, d_ff=16384)),
     # batches of 2048+ tokens take the lockstep fused kernel (smaller ones the per-token kernel)
     ("lockstep ragged T=2049", W.workload(2, T=2049)),
     ("lockstep C=T_n T=2080", dataclasses.replace(W.workload(2, T=2080, rho=0.3), slots=128)),
     ("lockstep c4 tail T=2100", W.workload(4, T=2100)),
+    ("lockstep wide d_ff=16384", W.workload(3, T=2048, d_model=512, d_ff=16384)),
 ]
 
 
