@@ -558,6 +558,18 @@ def main():
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": None if overridden or args.config != 3 else measured_traffic("fused_updown", src["fused_updown"], 1)}
 
+    # gather phase against the HBM peak: strictly required bytes, and the bytes the kernel moved past
+    # L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE of the current source, committed under profiles/)
+    fused_req_gbs = fused_bytes / (fused_ms * 1e-3) / 1e9
+    fused_info = {"required_hbm_gbs": round(fused_req_gbs, 1), "required_frac_of_hbm_peak": round(fused_req_gbs / PEAK_HBM_GBS, 4),
+                  "gathered_gbs": round(gathered_bytes / (fused_ms * 1e-3) / 1e9, 1),
+                  "gathered_bytes": int(gathered_bytes), "required_bytes": int(fused_bytes)}
+    past_l2 = None if overridden or args.config != 3 else measured_traffic("fused_updown", src["fused_updown"], 1)
+    if past_l2:
+        fused_past_gbs = past_l2 / (fused_ms * 1e-3) / 1e9
+        fused_info.update({"past_l2_bytes": int(past_l2), "past_l2_gbs": round(fused_past_gbs, 1),
+                           "past_l2_frac_of_hbm_peak": round(fused_past_gbs / PEAK_HBM_GBS, 4)})
+
     out = {
         "metric": "TwELL FFN tokens/sec at 99.5% act. sparsity; speedup vs dense; % roofline",
         "value": round(value, 1),
@@ -578,9 +590,7 @@ def main():
         "overflow_tiles": ovf,
         "phases_ms": {"gate_pack": round(pack_ms, 4), "fused_updown": round(fused_ms, 4)},
         "gate_pack_tflops": round(gate_flop / (pack_ms * 1e-3) / 1e12, 1),
-        "fused_updown": {"required_hbm_gbs": round(fused_bytes / (fused_ms * 1e-3) / 1e9, 1),
-                         "gathered_gbs": round(gathered_bytes / (fused_ms * 1e-3) / 1e9, 1),
-                         "gathered_bytes": int(gathered_bytes), "required_bytes": int(fused_bytes)},
+        "fused_updown": fused_info,
         "dense_ffn": dense,
         "classic_ell": classic,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 3) if dense else None,
