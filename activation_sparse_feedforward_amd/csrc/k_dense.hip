@@ -6,7 +6,7 @@
 // es el problema que TwELL resuelve?") and, for training, routes rows with too
 // many non-zeros to a dense fallback (section "¿Qué hace distinto a TwELL
 // frente a ELL clásico?").  Both use these two kernels:
-//   gateup: one GEMM whose 128-wide B tile is 64 gate rows + the same 64 up
+//   gateup: one GEMM whose 64-wide B tile is 32 gate rows + the same 32 up
 //           rows, so a lane holds g and u of the same (row, neuron) in
 //           matching accumulator registers; epilogue h = ReLU(g) * u;
 //   down:   y = h . W_down with W_down read [d_ff x d_model] (N contiguous)
@@ -31,19 +31,21 @@ __global__ __launch_bounds__(kThreads, 2) void gateup_kernel(GateUpArgs p) {
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.M;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   if (m0 >= n_rows) return;
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
+  // 32 neurons per workgroup: the fallback rows are few (one 256-row block at
+  // the training workload), so d_ff / 32 workgroups are what fills the chip
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 32;
 
   KRowLoader<E, kBM> la;
   la.init(p.x, p.d, m0, n_rows, p.rows);
   struct {
-    KRowLoader<E, 64> g, u;
+    KRowLoader<E, 32> g, u;
     __device__ void load(int kt) { g.load(kt); u.load(kt); }
-    __device__ void store(char* l, int) const { g.store(l, 0); u.store(l, 64); }
+    __device__ void store(char* l, int) const { g.store(l, 0); u.store(l, 32); }
   } lb;
   lb.g.init(p.w_gate_t, p.d, j0, p.F, nullptr);
   lb.u.init(p.w_up_t, p.d, j0, p.F, nullptr);
-  Acc<128> acc;
-  gemm_mainloop<E, 128>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
+  Acc<64> acc;
+  gemm_mainloop<E, 64>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
 
   const int lane = threadIdx.x & 63;
   const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
@@ -53,12 +55,9 @@ __global__ __launch_bounds__(kThreads, 2) void gateup_kernel(GateUpArgs p) {
     for (int r = 0; r < 16; ++r) {
       const int64_t m = wrow0 + mb * 32 + acc_row(r, lane);
       if (m >= n_rows) continue;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float g = acc.c[mb][nb][r];
-        const float h = (g > 0.f ? g : 0.f) * acc.c[mb][nb + 2][r];
-        store_bits<E>(p.h, m * p.F + j0 + nb * 32 + (lane & 31), round_store<E>(h).bits);
-      }
+      const float g = acc.c[mb][0][r];
+      const float h = (g > 0.f ? g : 0.f) * acc.c[mb][1][r];
+      store_bits<E>(p.h, m * p.F + j0 + (lane & 31), round_store<E>(h).bits);
     }
   }
 }
@@ -259,8 +258,8 @@ hipError_t launch_dense256(const GateUpArgs& g, const DownArgs& dn, int dtype, h
 
 template <class E>
 static hipError_t launch_gateup_t(const GateUpArgs& a, hipStream_t s) {
-  dim3 grid(a.F / 64, static_cast<unsigned>((a.M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gateup_kernel<E>), grid, dim3(kThreads), (kBM + 128) * 128, s, a);
+  dim3 grid(a.F / 32, static_cast<unsigned>((a.M + kBM - 1) / kBM));
+  hipLaunchKernelGGL((gateup_kernel<E>), grid, dim3(kThreads), (kBM + 64) * 128, s, a);
   return hipGetLastError();
 }
 
