@@ -13,7 +13,7 @@
 //        (both operands MN-contiguous, K = n_dense, fp32 read-modify-write on
 //        top of the sparse rows' contribution written before)
 // The dense rows are few (n_dense ~ 250 of 16384 at the training workload), so
-// the three products share one launch of 3 x d_ff/128 workgroups instead of
+// the three products share one launch of 3 x d_ff/64 workgroups instead of
 // leaving most of the chip idle in two smaller ones.
 #include "gemm_core.hpp"
 #include "internal.hpp"
@@ -46,13 +46,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gue_kernel(BwdArgs p) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   if (m0 >= n) return;
   const int z = blockIdx.z;
-  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64;
   KRowLoader<E, kBM> la;
   la.init(z == 2 ? p.dy : p.x, p.d, m0, n, p.dense_rows);
-  KRowLoader<E, 128> lb;
+  KRowLoader<E, 64> lb;
   lb.init(z == 0 ? p.w_gate_t : (z == 1 ? p.w_up_t : p.w_down), p.d, j0, p.F, nullptr);
-  Acc<128> acc;
-  gemm_mainloop<E, 128>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
+  Acc<64> acc;
+  gemm_mainloop<E, 64>(la, lb, p.d / KRowLoader<E, kBM>::kSliceElems, lds, acc);
   float* out = z == 0 ? p.g_d : (z == 1 ? p.u_d : p.e_d);
   const int lane = threadIdx.x & 63;
   const int64_t wrow0 = m0 + (threadIdx.x >> 6) * 64;
@@ -63,10 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_gue_kernel(BwdArgs p) {
       const int64_t m = wrow0 + mb * 32 + acc_row(r, lane);
       if (m >= n) continue;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t j = j0 + nb * 32 + (lane & 31);
-        if (j < p.F) out[m * p.F + j] = acc.c[mb][nb][r];  // d_ff need only be a multiple of 64
-      }
+      for (int nb = 0; nb < 2; ++nb) out[m * p.F + j0 + nb * 32 + (lane & 31)] = acc.c[mb][nb][r];
     }
 }
 
@@ -174,7 +171,7 @@ template <class E>
 static hipError_t launch_bwd_dense_t(const BwdArgs& a, hipStream_t s) {
   const unsigned mrows = static_cast<unsigned>((a.cap + kBM - 1) / kBM);
   const size_t lds = (kBM + 128) * 128;
-  hipLaunchKernelGGL((bwd_gue_kernel<E>), dim3((a.F + 127) / 128, mrows, 3), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((bwd_gue_kernel<E>), dim3(a.F / 64, mrows, 3), dim3(kThreads), (kBM + 64) * 128, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t quads = a.cap * a.F / 4;
