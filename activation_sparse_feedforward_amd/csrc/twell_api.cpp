@@ -443,7 +443,7 @@ const char* twell_status_str(twell_status s) {
   switch (s) {
     case TWELL_OK: return "ok";
     case TWELL_EINVAL: return "invalid argument (descriptor, pointer, alignment or workspace size)";
-    case TWELL_EUNSUPPORTED: return "shape or dtype not supported by this build";
+    case TWELL_EUNSUPPORTED: return "shape or dtype not supported by the library";
     case TWELL_EHIP: return "HIP launch error";
   }
   return "unknown status";

@@ -37,7 +37,7 @@
  *    validation and the kernel launches, with no host synchronisation.
  *  - Errors: TWELL_EINVAL for a bad descriptor, NULL / misaligned pointer or
  *    too-small workspace (nothing is launched); TWELL_EUNSUPPORTED for a valid
- *    shape this build has no kernel for; TWELL_EHIP when a launch fails.
+ *    shape the library has no kernel for; TWELL_EHIP when a launch fails.
  *    Data-dependent conditions (overflowing tiles, dense-row cap exceeded) are
  *    reported in device counters, never as host errors.
  *  - Supported shapes: dtype BF16 with d_model % 512 == 0 and d_model <= 4096,
