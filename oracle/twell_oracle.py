@@ -28,7 +28,7 @@ The method reaches the dense result exactly (only faster), so this oracle *is*
 the plain dense gated FFN, plus a packer/unpacker, a router and a manual
 backward.
 
-Conventions (readings where the pages are silent, all listed in the design doc):
+Conventions (readings where the pages are silent):
   * Weights are stored one row per neuron: W_gate^T, W_up^T, W_down are each
     [d_ff x d_model] row-major, so g = x @ W_gate^T.T, y = h @ W_down.
   * Arithmetic is float64 throughout; the pages fix no precision.  Inputs are
