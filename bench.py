@@ -108,9 +108,11 @@ def _pmc_per_dispatch(path: str, counter: str):
     return {k: (sum(d.values()) / len(d), len(d)) for k, d in vals.items()}
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str):
+def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str, out_dir: str | None = None):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same counters
-    read for the calibration copy of known size, and store bytes per launch."""
+    read for the calibration copy of known size, and store bytes per launch
+    (as traffic_<kernel>.json in out_dir, by default profiles/)."""
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
     if "calib_copy" not in fetch or "calib_copy" not in write:
@@ -132,7 +134,7 @@ def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str
                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
                "read_bytes_per_launch": int(rb), "write_bytes_per_launch": int(wb),
                "bytes_per_launch": int(rb + wb), "command": command}
-        with open(os.path.join(ROOT, "profiles", f"traffic_{key}.json"), "w") as fh:
+        with open(os.path.join(out_dir, f"traffic_{key}.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
             fh.write("\n")
         out[key] = rec
