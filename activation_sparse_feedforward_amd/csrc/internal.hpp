@@ -37,6 +37,9 @@ struct FusedArgs {
   int32_t groups;
   float* part;
   int64_t part_rows;
+  // lockstep start barrier (set by the launcher)
+  uint32_t epoch;
+  int32_t resident;
 };
 
 // Classic ELL construction (baseline): dense ReLU(g) [T x F] written to `dense`,
@@ -154,6 +157,8 @@ struct BwdArgs {
   int64_t heavy_cap;
   int32_t groups;        // tile ranges per heavy row
   float* dx_hpart;       // [groups][heavy_cap][d] fp32 partial dx of the heavy rows
+  uint32_t epoch;        // lockstep start barrier of the dx pass (set by the launcher)
+  int32_t resident;
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -176,5 +181,10 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, const 
                                 const int32_t* rows, void* out, int d, int dtype, hipStream_t s);
 hipError_t launch_bwd_sparse(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_bwd_dense(const BwdArgs& a, int dtype, hipStream_t s);
+
+// Lockstep launches: a fresh epoch for the start-barrier counters, and the
+// number of workgroups of one lockstep kernel the current device holds at once.
+uint32_t lockstep_epoch();
+int lockstep_resident();
 
 }  // namespace twell

@@ -477,8 +477,12 @@ constexpr int kDxChunkMax = 4;    // 4 tiles x 128 neurons x 2 rows x 4 KB = 4 M
 
 constexpr size_t bwd_dx_sync_lds_bytes() { return static_cast<size_t>(kDxWaves) * kDxList * 16; }
 
+// start-barrier counters of the lockstep dx pass (per device; see lockstep_start_barrier)
+__device__ unsigned long long g_dx_start[kStartCounters * kStartCounterStride];
+
 template <class E, int NV, int TPW, int kC>
 __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdArgs p) {
+  lockstep_start_barrier(g_dx_start, p.epoch, p.resident);
   constexpr int kN = VecB<E>::N;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63;
@@ -604,7 +608,10 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
 }
 
 template <class E, int NV, int TPW, int kC>
-static hipError_t launch_bwd_dx_sync_c(const BwdArgs& a, hipStream_t s) {
+static hipError_t launch_bwd_dx_sync_c(const BwdArgs& args, hipStream_t s) {
+  BwdArgs a = args;
+  a.epoch = lockstep_epoch();
+  a.resident = lockstep_resident();
   constexpr size_t lds = bwd_dx_sync_lds_bytes();
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),

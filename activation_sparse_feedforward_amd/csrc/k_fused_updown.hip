@@ -276,8 +276,12 @@ constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
 
+// start-barrier counters of the lockstep kernel (per device; see lockstep_start_barrier)
+__device__ unsigned long long g_fused_start[kStartCounters * kStartCounterStride];
+
 template <class E, int NV, int TPW, int kU, int kC>
 __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
+  lockstep_start_barrier(g_fused_start, p.epoch, p.resident);
   constexpr int kN = Vec<E>::N;
   constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
   extern __shared__ __align__(16) char smem[];
@@ -603,8 +607,11 @@ constexpr size_t sync_lds_bytes() {
 }
 
 template <class E, int NV, int TPW, int kU>
-static hipError_t launch_sync_cfg(const FusedArgs& a, hipStream_t s) {
+static hipError_t launch_sync_cfg(const FusedArgs& args, hipStream_t s) {
   constexpr size_t lds = sync_lds_bytes<NV, TPW, E::kBytes>();
+  FusedArgs a = args;
+  a.epoch = lockstep_epoch();
+  a.resident = lockstep_resident();
   const int64_t per_block = static_cast<int64_t>(kSyncWaves) * TPW;
   dim3 grid(static_cast<unsigned>((a.T + per_block - 1) / per_block));
   if constexpr (E::kBytes == 2) {

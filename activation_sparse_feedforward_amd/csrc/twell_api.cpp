@@ -3,6 +3,7 @@
 // the device and can be tested without a GPU.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "../../include/twell.h"
@@ -135,6 +136,35 @@ BwdWs bwd_ws(const twell_desc* d, int64_t max_dense_rows) {
 twell_status from_hip(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_EHIP; }
 
 }  // namespace
+
+namespace twell {
+
+// Epochs of the lockstep start-barrier counters: every lockstep launch takes a
+// new one (0 is never used, so the zero-initialised counters start empty).
+uint32_t lockstep_epoch() {
+  static std::atomic<uint32_t> epoch{0};
+  uint32_t e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (e == 0) e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e;
+}
+
+// One lockstep workgroup per CU (their LDS or VGPR footprint); 0 turns the
+// start barrier off when the device cannot be queried.
+int lockstep_resident() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace twell
 
 extern "C" {
 
