@@ -507,7 +507,10 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   // list builder lanes: lane = tile_in_chunk * TPW + row
   const int chunk_tiles = max(1, min(min(kWave / TPW, kDxList / (C * TPW)), kDxChunkMax));
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
-  const int rot = static_cast<int>(blockIdx.x & 7) * (n_chunks / 8);
+  // a later generation starts one chunk earlier than the one before it, on the
+  // chunk its XCD's previous generation swept last (still in L2)
+  const int gen_r = p.resident > 0 ? static_cast<int>(blockIdx.x) / p.resident : 0;
+  const int rot = ((static_cast<int>(blockIdx.x & 7) * (n_chunks / 8) - gen_r) % n_chunks + n_chunks) % n_chunks;
   const int kl = lane % TPW;
   int my_tok = 0;  // token rows are < 2^31
   bool my_act = false;
