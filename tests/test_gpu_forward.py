@@ -197,6 +197,18 @@ def test_full_size_sampled_rows(cfg):
     _check_case(w, rows=_sample_rows(w.T, cfg), label=f"full c{cfg}")
 
 
+def test_lockstep_three_generations_sampled():
+    """24 608 tokens (d_model = 512): 769 lockstep workgroups of 32 rows, i.e.
+    three generations on 256 CUs and a ragged fourth of one workgroup, so the
+    start barrier of every later generation and its rotation shift run; rows
+    around each generation boundary are checked."""
+    w = W.workload(3, T=24608, d_model=512)
+    rows = set(_sample_rows(w.T, 11).tolist())
+    for b in (8192, 16384, 24576):
+        rows |= set(range(b - 64, min(b + 64, w.T)))
+    _check_case(w, rows=np.array(sorted(rows)), label="three generations")
+
+
 def test_dense_ffn_full_size_sampled():
     """The dense FFN in the configuration the benchmark times (2B-class shape,
     T=16384), checked on sampled rows against the float64 dense FFN."""
