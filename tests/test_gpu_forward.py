@@ -194,7 +194,12 @@ def test_full_size_sampled_rows(cfg):
     """Full workload sizes, the launch configuration the benchmark times;
     float64 checks on sampled rows (first and last M tiles plus random rows)."""
     w = W.workload(cfg)
-    _check_case(w, rows=_sample_rows(w.T, cfg), label=f"full c{cfg}")
+    r, _ = _check_case(w, rows=_sample_rows(w.T, cfg), label=f"full c{cfg}")
+    # two generations of lockstep workgroups at c3: a second call gives the same bits
+    y2 = poison_(torch.empty_like(r["y"]))
+    T.twell_ffn_fwd(desc_for(w), r["x"], r["act"], r["wu"], r["wd"], y2)
+    torch.cuda.synchronize()
+    assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
 
 
 def test_lockstep_three_generations_sampled():
