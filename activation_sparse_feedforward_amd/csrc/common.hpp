@@ -54,47 +54,6 @@ template <> __device__ __forceinline__ Rounded<EF32> round_store<EF32>(float v) 
   return {__float_as_uint(v), v};
 }
 
-// Start barrier of the lockstep kernels' later generations.  `resident` is
-// the number of workgroups the chip holds at once (one per CU); workgroup b is
-// dealt to XCD b mod 8.  The workgroups of generation g >= 1 start as those of
-// generation g - 1 finish, spread over tens of microseconds, and a late starter
-// would trail its XCD's peers through the whole tile sweep, fetching weight
-// rows they have already evicted from L2.  So each of them arrives at the
-// counter of its (generation, XCD) group and waits, for at most 100 us, until
-// the group is complete.  A counter carries the launch's epoch in its high
-// half: no launch has to clear it, and a counter left by another launch counts
-// as empty.  The wait only paces the sweep: on a timeout the workgroup goes
-// on, and no result depends on it.
-constexpr int kStartCounters = 256;      // (generation, XCD) groups; later ones wrap around
-constexpr int kStartCounterStride = 16;  // 128 bytes between counters
-
-__device__ __forceinline__ void lockstep_start_barrier(unsigned long long* ctrs, uint32_t epoch, int resident) {
-  if (resident <= 0 || static_cast<int>(blockIdx.x) < resident) return;
-  const int gen = static_cast<int>(blockIdx.x) / resident;
-  const int xcc = static_cast<int>(blockIdx.x) & 7;
-  const int lo = gen * resident, hi = min(lo + resident, static_cast<int>(gridDim.x));
-  const uint32_t size = static_cast<uint32_t>((hi - lo - xcc + 7) / 8);
-  unsigned long long* c = ctrs + ((gen * 8 + xcc) % kStartCounters) * kStartCounterStride;
-  if (threadIdx.x == 0) {
-    const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
-    unsigned long long old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int k = 0; k < 1024; ++k) {
-      const unsigned long long want = (old >> 32) == epoch ? old + 1ull : (tag | 1ull);
-      if (__hip_atomic_compare_exchange_strong(c, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    const unsigned long long deadline = __builtin_amdgcn_s_memrealtime() + 10000;  // 100 MHz clock
-    for (int it = 0; it < 100000; ++it) {
-      const unsigned long long v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((v >> 32) == epoch && static_cast<uint32_t>(v) >= size) break;
-      __builtin_amdgcn_s_sleep(2);
-      if (__builtin_amdgcn_s_memrealtime() > deadline) break;
-    }
-  }
-  __syncthreads();
-}
-
 template <class E> __device__ __forceinline__ void store_bits(void* p, int64_t i, uint32_t bits);
 template <> __device__ __forceinline__ void store_bits<EBf16>(void* p, int64_t i, uint32_t bits) {
   static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(bits);

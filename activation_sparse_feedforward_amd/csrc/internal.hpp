@@ -37,9 +37,10 @@ struct FusedArgs {
   int32_t groups;
   float* part;
   int64_t part_rows;
-  // lockstep start barrier (set by the launcher)
-  uint32_t epoch;
+  // lockstep launches (set by the launcher): workgroups the device runs at
+  // once, and the first row block of this launch
   int32_t resident;
+  int64_t blk0;
 };
 
 // Classic ELL construction (baseline): dense ReLU(g) [T x F] written to `dense`,
@@ -157,8 +158,8 @@ struct BwdArgs {
   int64_t heavy_cap;
   int32_t groups;        // tile ranges per heavy row
   float* dx_hpart;       // [groups][heavy_cap][d] fp32 partial dx of the heavy rows
-  uint32_t epoch;        // lockstep start barrier of the dx pass (set by the launcher)
-  int32_t resident;
+  int32_t resident;      // lockstep dx pass (set by the launcher): workgroups run at once,
+  int64_t blk0;          // and the first row block of this launch
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Each returns hipSuccess or the launch error.
@@ -182,9 +183,8 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, const 
 hipError_t launch_bwd_sparse(const BwdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_bwd_dense(const BwdArgs& a, int dtype, hipStream_t s);
 
-// Lockstep launches: a fresh epoch for the start-barrier counters, and the
-// number of workgroups of one lockstep kernel the current device holds at once.
-uint32_t lockstep_epoch();
+// Lockstep launches: how many workgroups of one lockstep kernel (one per CU)
+// the current device runs at once; 0 if it cannot be queried.
 int lockstep_resident();
 
 }  // namespace twell

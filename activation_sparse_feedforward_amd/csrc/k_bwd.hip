@@ -477,12 +477,8 @@ constexpr int kDxChunkMax = 4;    // 4 tiles x 128 neurons x 2 rows x 4 KB = 4 M
 
 constexpr size_t bwd_dx_sync_lds_bytes() { return static_cast<size_t>(kDxWaves) * kDxList * 16; }
 
-// start-barrier counters of the lockstep dx pass (per device; see lockstep_start_barrier)
-__device__ unsigned long long g_dx_start[kStartCounters * kStartCounterStride];
-
 template <class E, int NV, int TPW, int kC>
 __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdArgs p) {
-  lockstep_start_barrier(g_dx_start, p.epoch, p.resident);
   constexpr int kN = VecB<E>::N;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63;
@@ -491,12 +487,14 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
   const int64_t n_rows = p.split_n[0];
+  const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
+  if (blk * kDxWaves * TPW >= n_rows) return;  // the whole workgroup is past the rows
   int64_t tk[TPW];
   bool act[TPW];
   float dxf[TPW][NV][kN];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int64_t i_row = (static_cast<int64_t>(blockIdx.x) * kDxWaves + wave) * TPW + k;
+    const int64_t i_row = (blk * kDxWaves + wave) * TPW + k;
     act[k] = i_row < n_rows;  // idle rows: the wave still takes part in the barriers
     tk[k] = act[k] ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.light_rows[i_row])) : 0;
 #pragma unroll
@@ -509,8 +507,8 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
   // a later generation starts one chunk earlier than the one before it, on the
   // chunk its XCD's previous generation swept last (still in L2)
-  const int gen_r = p.resident > 0 ? static_cast<int>(blockIdx.x) / p.resident : 0;
-  const int rot = ((static_cast<int>(blockIdx.x & 7) * (n_chunks / 8) - gen_r) % n_chunks + n_chunks) % n_chunks;
+  const int gen_r = p.resident > 0 ? static_cast<int>(blk / p.resident) : 0;
+  const int rot = ((static_cast<int>(blk & 7) * (n_chunks / 8) - gen_r) % n_chunks + n_chunks) % n_chunks;
   const int kl = lane % TPW;
   int my_tok = 0;  // token rows are < 2^31
   bool my_act = false;
@@ -613,7 +611,6 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
 template <class E, int NV, int TPW, int kC>
 static hipError_t launch_bwd_dx_sync_c(const BwdArgs& args, hipStream_t s) {
   BwdArgs a = args;
-  a.epoch = lockstep_epoch();
   a.resident = lockstep_resident();
   constexpr size_t lds = bwd_dx_sync_lds_bytes();
   static const hipError_t attr =
@@ -621,10 +618,18 @@ static hipError_t launch_bwd_dx_sync_c(const BwdArgs& args, hipStream_t s) {
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
   constexpr int64_t per_block = static_cast<int64_t>(kDxWaves) * TPW;
-  hipLaunchKernelGGL((bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
-                     dim3(static_cast<unsigned>((a.T + per_block - 1) / per_block)), dim3(kDxWaves * kWave), lds, s,
-                     a);
-  return hipGetLastError();
+  const int64_t blocks = (a.T + per_block - 1) / per_block;
+  // one launch per generation of resident workgroups (as the forward's lockstep kernel)
+  const int64_t step = a.resident > 0 ? a.resident : blocks;
+  for (int64_t b0 = 0; b0 < blocks; b0 += step) {
+    a.blk0 = b0;
+    hipLaunchKernelGGL((bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
+                       dim3(static_cast<unsigned>(blocks - b0 < step ? blocks - b0 : step)), dim3(kDxWaves * kWave), lds,
+                       s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 // Rows per wave: two fp32 dx rows beside one pair's two weight rows fit the
 // 128 VGPRs of a 16-wave workgroup up to d_model = 2048 (bf16) / 1024 (fp32);

@@ -276,12 +276,8 @@ constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
 
-// start-barrier counters of the lockstep kernel (per device; see lockstep_start_barrier)
-__device__ unsigned long long g_fused_start[kStartCounters * kStartCounterStride];
-
 template <class E, int NV, int TPW, int kU, int kC>
 __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
-  lockstep_start_barrier(g_fused_start, p.epoch, p.resident);
   constexpr int kN = Vec<E>::N;
   constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
   extern __shared__ __align__(16) char smem[];
@@ -290,6 +286,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
+  const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
+  if (blk * kSyncWaves * TPW >= n_rows) return;  // the whole workgroup is past the rows
   int4* list = list_all + wave * kSyncList;
   u32x4_t* xw = xl + wave * TPW * kRowVec;
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
@@ -300,7 +298,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   float yf[TPW][NV][kN];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int64_t i_row = (static_cast<int64_t>(blockIdx.x) * kSyncWaves + wave) * TPW + k;
+    const int64_t i_row = (blk * kSyncWaves + wave) * TPW + k;
     act[k] = i_row < n_rows;  // idle tokens: the wave still takes part in the barriers
     // wave-uniform: keep the token rows in scalar registers
     tk[k] = act[k] ? (p.rows ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.rows[i_row])) : i_row) : 0;
@@ -325,8 +323,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
   // a later generation starts one chunk earlier than the one before it, on the
   // chunk its XCD's previous generation swept last (still in L2)
-  const int gen_r = p.resident > 0 ? static_cast<int>(blockIdx.x) / p.resident : 0;
-  const int rot = ((static_cast<int>(blockIdx.x & 7) * (n_chunks / 8) - gen_r) % n_chunks + n_chunks) % n_chunks;
+  const int gen_r = p.resident > 0 ? static_cast<int>(blk / p.resident) : 0;
+  const int rot = ((static_cast<int>(blk & 7) * (n_chunks / 8) - gen_r) % n_chunks + n_chunks) % n_chunks;
   const int kl = lane % TPW;
   int my_tok = 0;  // token rows are < 2^31
   bool my_act = false;
@@ -613,28 +611,36 @@ template <class E, int NV, int TPW, int kU>
 static hipError_t launch_sync_cfg(const FusedArgs& args, hipStream_t s) {
   constexpr size_t lds = sync_lds_bytes<NV, TPW, E::kBytes>();
   FusedArgs a = args;
-  a.epoch = lockstep_epoch();
   a.resident = lockstep_resident();
   const int64_t per_block = static_cast<int64_t>(kSyncWaves) * TPW;
-  dim3 grid(static_cast<unsigned>((a.T + per_block - 1) / per_block));
-  if constexpr (E::kBytes == 2) {
-    if (a.C == 16) {
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 16>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      if (attr != hipSuccess) return attr;
-      hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 16>), grid, dim3(kSyncWaves * kWave), lds, s, a);
-      return hipGetLastError();
+  const int64_t blocks = (a.T + per_block - 1) / per_block;
+  // one launch per generation of resident workgroups, so every generation
+  // starts on a free chip, its workgroups together
+  const int64_t step = a.resident > 0 ? a.resident : blocks;
+  for (int64_t b0 = 0; b0 < blocks; b0 += step) {
+    a.blk0 = b0;
+    dim3 grid(static_cast<unsigned>(blocks - b0 < step ? blocks - b0 : step));
+    if constexpr (E::kBytes == 2) {
+      if (a.C == 16) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 16>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (attr != hipSuccess) return attr;
+        hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 16>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        continue;
+      }
     }
-  }
-  {
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 0>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 0>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 // Tokens per wave: as many fp32 y rows as fit beside the loads in 128 VGPRs,

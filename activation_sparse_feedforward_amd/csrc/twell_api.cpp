@@ -139,15 +139,6 @@ twell_status from_hip(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_
 
 namespace twell {
 
-// Epochs of the lockstep start-barrier counters: every lockstep launch takes a
-// new one (0 is never used, so the zero-initialised counters start empty).
-uint32_t lockstep_epoch() {
-  static std::atomic<uint32_t> epoch{0};
-  uint32_t e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  if (e == 0) e = epoch.fetch_add(1, std::memory_order_relaxed) + 1;
-  return e;
-}
-
 // One lockstep workgroup per CU (their LDS or VGPR footprint); 0 turns the
 // start barrier off when the device cannot be queried.
 int lockstep_resident() {

@@ -120,15 +120,19 @@ def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str
     known = calib_mib * 1024 * 1024
     f_fac = known / (fetch["calib_copy"][0] * 1024)
     w_fac = known / (write["calib_copy"][0] * 1024)
+    # one step calls twell_pack (one gate dispatch) and twell_ffn_fwd (one dispatch per generation of
+    # lockstep workgroups), so the bytes of a call are a kernel's total over the gate dispatch count
+    calls = fetch["gate_pack"][1] if "gate_pack" in fetch else None
     out = {}
     for key in KERNEL_SOURCES:
         if key not in fetch or key not in write:
             continue
-        rb = fetch[key][0] * 1024 * f_fac
-        wb = write[key][0] * 1024 * w_fac
+        n_call = calls or fetch[key][1]
+        rb = fetch[key][0] * fetch[key][1] / n_call * 1024 * f_fac
+        wb = write[key][0] * write[key][1] / n_call * 1024 * w_fac
         rec = {"kernel": key, "source_hash": kernel_source_hash(KERNEL_SOURCES[key]),
                "fetch_kib_per_dispatch": round(fetch[key][0], 1), "write_kib_per_dispatch": round(write[key][0], 1),
-               "dispatches": [fetch[key][1], write[key][1]],
+               "dispatches": [fetch[key][1], write[key][1]], "calls": n_call,
                "calib_copy_bytes": known, "calib_fetch_kib": round(fetch["calib_copy"][0], 1),
                "calib_write_kib": round(write["calib_copy"][0], 1),
                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),

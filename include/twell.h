@@ -31,12 +31,7 @@
  *    (stored) value is not zero.
  *  - Pointers: every array argument is a DEVICE pointer, 16-byte aligned,
  *    owned by the caller.  The library never allocates or frees memory and
- *    keeps no state that a result depends on; scratch memory is passed in as
- *    `ws`.  (The lockstep kernels of twell_ffn_fwd, twell_ffn_fwd_hybrid and
- *    twell_ffn_bwd pace the start of their later workgroups with counters in
- *    the library's own static device memory, 32 KB per kernel and device,
- *    tagged with a per-launch epoch; concurrent launches on one device may
- *    slow each other's pacing, never change a result.)
+ *    keeps no state between calls; scratch memory is passed in as `ws`.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default
  *    stream).  All calls are asynchronous: they return after host-side
  *    validation and the kernel launches, with no host synchronisation.
@@ -49,8 +44,8 @@
  *    or FP32 with d_model % 256 == 0 and d_model <= 2048; tile_n in {64, 128};
  *    d_ff % tile_n == 0; 1 <= slots <= tile_n; T >= 0 (T == 0 is a no-op);
  *    T * max(d_model, d_ff) < 2^31.
- *  - Threading: calls are thread-safe (the only host-side shared state is an
- *    atomic epoch counter and a per-device cache of the CU count).
+ *  - Threading: calls are thread-safe (the only shared state is a per-device
+ *    cache of the CU count, held in atomics).
  */
 #ifndef TWELL_H
 #define TWELL_H

@@ -36,11 +36,17 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path):
     fetch = [(1, "neg_kernel(float*)", [mib * 1024 / 2 / 4] * 4),
              (2, "void twell::gate_pack256_kernel<...>(PackArgs)", [1000.0, 1000.0]),
              (3, "void twell::gate_pack256_kernel<...>(PackArgs)", [3000.0, 3000.0]),
-             (4, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [500.0])]
+             (4, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [500.0]),
+             (5, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [300.0]),
+             (6, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [500.0]),
+             (7, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [300.0])]
     write = [(1, "neg_kernel(float*)", [mib * 1024 / 4] * 4),
              (2, "void twell::gate_pack256_kernel<...>(PackArgs)", [10.0]),
              (3, "void twell::gate_pack256_kernel<...>(PackArgs)", [30.0]),
-             (4, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [7.0])]
+             (4, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [7.0]),
+             (5, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [3.0]),
+             (6, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [7.0]),
+             (7, "void twell::fused_updown_sync_kernel<...>(FusedArgs)", [3.0])]
     f, w = tmp_path / "f.csv", tmp_path / "w.csv"
     _counter_csv(f, "FETCH_SIZE", fetch)
     _counter_csv(w, "WRITE_SIZE", write)
@@ -53,5 +59,8 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path):
     assert g["write_bytes_per_launch"] == int(20 * 1024)
     assert g["dispatches"] == [2, 2]
     assert g["source_hash"] == bench.kernel_source_hash(bench.KERNEL_SOURCES["gate_pack"])
+    # two fused dispatches per call (one per generation of workgroups): bytes per call sum them
     u = json.loads((tmp_path / "traffic_fused_updown.json").read_text())
-    assert u["bytes_per_launch"] == int(500 * 1024 * 2.0) + int(7 * 1024)
+    assert u["calls"] == 2
+    assert u["read_bytes_per_launch"] == int(800 * 1024 * 2.0)
+    assert u["write_bytes_per_launch"] == int(10 * 1024)
