@@ -135,9 +135,14 @@ twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t
 twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
                                 void* ws, size_t ws_bytes, void* stream);
 
-/* Fused up + down projection on TwELL input, in ONE kernel dispatch.
+/* Fused up + down projection on TwELL input, in ONE fused kernel.
  * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down
  * projections together; the intermediate never reaches global memory.]
+ * Batches of 2048 rows and more take the lockstep kernel, launched once per
+ * generation of workgroups the device runs at once (one per CU, 32 rows each:
+ * two launches at 16384 rows on 256 CUs) on disjoint row blocks, so each
+ * generation starts together; every row is still computed start to finish by
+ * one workgroup of one launch. */
  * For every row t and stored slot (neuron j = b*tile_n + idx, value a):
  *   u = x[t] . w_up_t[j];  h = a * u;  y[t] += h * w_down[j]   (fp32 accumulate)
  * y [T x d_model] is overwritten (stored in dtype).  A tile with count > slots
