@@ -142,7 +142,7 @@ twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* 
  * generation of workgroups the device runs at once (one per CU, 32 rows each:
  * two launches at 16384 rows on 256 CUs) on disjoint row blocks, so each
  * generation starts together; every row is still computed start to finish by
- * one workgroup of one launch. */
+ * one workgroup of one launch.
  * For every row t and stored slot (neuron j = b*tile_n + idx, value a):
  *   u = x[t] . w_up_t[j];  h = a * u;  y[t] += h * w_down[j]   (fp32 accumulate)
  * y [T x d_model] is overwritten (stored in dtype).  A tile with count > slots
