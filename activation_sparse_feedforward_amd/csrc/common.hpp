@@ -35,6 +35,44 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// y += c * w over one 16-byte piece of a row held in storage form, y in fp32.
+// bf16: c is rounded to bf16 once (the precision in which a dense bf16 path
+// stores the hidden activations and their gradients before the next
+// product) and every element is a packed-pair dot product of the row's bf16
+// pair with (c, 0) or (0, c): the product of two bf16 values is exact in
+// fp32, so each element still takes one fp32 rounding, and the row needs no
+// unpacking.  fp32: plain FMAs.  (The 16-byte vector is bit-cast whole to
+// bf16x8 before taking pairs: casting an element of the 32-bit vector
+// directly was compiled to always read element 0.)
+template <class E> struct AxpyCoef;
+template <> struct AxpyCoef<EBf16> {
+  bf16x2_t lo, hi;  // (c, 0) and (0, c)
+  __device__ __forceinline__ explicit AxpyCoef(float c) {
+    const uint32_t b = f32_to_bf16_bits(c);
+    lo = __builtin_bit_cast(bf16x2_t, b);
+    hi = __builtin_bit_cast(bf16x2_t, b << 16);
+  }
+  __device__ __forceinline__ void axpy(const u32x4_t& w, float* y) const {
+    const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2_t pr{wh[2 * i], wh[2 * i + 1]};
+      y[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, lo, y[2 * i], false);
+      y[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, hi, y[2 * i + 1], false);
+    }
+  }
+};
+template <> struct AxpyCoef<EF32> {
+  float c;
+  __device__ __forceinline__ explicit AxpyCoef(float v) : c(v) {}
+  __device__ __forceinline__ void axpy(const u32x4_t& w, float* y) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = fmaf(c, __uint_as_float(w[i]), y[i]);
+  }
+};
+
 template <class E> __device__ __forceinline__ float load_elem(const void* p, int64_t i);
 template <> __device__ __forceinline__ float load_elem<EBf16>(const void* p, int64_t i) {
   return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);

@@ -108,8 +108,6 @@ template <> struct VecB<EF32> {
   }
 };
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 // Per-lane partial dot product of two rows held as NV 16-byte vectors; bf16
 // pairs go through v_dot2c_f32_bf16 (fp32 accumulate) without unpacking, in
 // four interleaved partial sums.  (The 16-byte vector is bit-cast whole to
@@ -326,17 +324,12 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
       const float du = dh * a;
       const float dg = dh * u;
       if (e0 + q < end && lane == 0) p.coef[sq[q]] = make_float2(dg, du);
+      const AxpyCoef<E> cg(dg), cu(du), ch(h);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        float xf[kN], yf[kN];
-        VecB<E>::unpack(xv[q][v], xf);
-        VecB<E>::unpack(yv[q][v], yf);
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          ag[v][i] = fmaf(dg, xf[i], ag[v][i]);
-          au[v][i] = fmaf(du, xf[i], au[v][i]);
-          ad[v][i] = fmaf(h, yf[i], ad[v][i]);
-        }
+        cg.axpy(xv[q][v], ag[v]);
+        cu.axpy(xv[q][v], au[v]);
+        ch.axpy(yv[q][v], ad[v]);
       }
     }
   }
@@ -439,13 +432,11 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_ell_dx_kernel(BwdArg
       }
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
+        const AxpyCoef<E> cg(cf[q].x), cu(cf[q].y);
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-          float w1[kN], w3[kN];
-          VecB<E>::unpack(wu[q][v], w1);
-          VecB<E>::unpack(wg[q][v], w3);
-#pragma unroll
-          for (int i = 0; i < kN; ++i) dxf[v][i] = fmaf(cf[q].x, w3[i], fmaf(cf[q].y, w1[i], dxf[v][i]));
+          cu.axpy(wu[q][v], dxf[v]);
+          cg.axpy(wg[q][v], dxf[v]);
         }
       }
     }
@@ -585,13 +576,11 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
 #pragma unroll
       for (int k = 0; k < TPW; ++k) {
         if (kk == k) {  // wave-uniform
+          const AxpyCoef<E> cg(cf.x), cu(cf.y);
 #pragma unroll
           for (int v = 0; v < NV; ++v) {
-            float w1[kN], w3[kN];
-            VecB<E>::unpack(wu[v], w1);
-            VecB<E>::unpack(wg[v], w3);
-#pragma unroll
-            for (int i = 0; i < kN; ++i) dxf[k][v][i] = fmaf(cf.x, w3[i], fmaf(cf.y, w1[i], dxf[k][v][i]));
+            cu.axpy(wu[v], dxf[k][v]);
+            cg.axpy(wg[v], dxf[k][v]);
           }
         }
       }

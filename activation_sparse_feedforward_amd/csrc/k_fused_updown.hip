@@ -73,8 +73,6 @@ template <> struct Vec<EF32> {
   }
 };
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 // This lane's part of the dot product of two rows held as NV 16-byte chunks
 // (x and w in storage form).  bf16: packed-pair dot products (v_dot2 with an
 // fp32 accumulator) in four independent chains, summed at the end; fp32:
@@ -116,40 +114,6 @@ __device__ __forceinline__ void lane_dot_piece(const u32x4_t& w, const u32x4_t& 
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(__uint_as_float(w[i]), __uint_as_float(x[i]), acc[i]);
   }
 }
-
-// y += h * w over one 16-byte piece of a W_down row (storage form), y in
-// fp32.  bf16: h is rounded to bf16 once per neuron (the precision in which a
-// dense bf16 FFN hands its hidden activations to the down projection) and
-// every element is a packed-pair dot product of the row's bf16 pair with
-// (h, 0) or (0, h): the product of two bf16 values is exact in fp32, so each
-// element still takes one fp32 rounding, and the row needs no unpacking.
-// fp32: plain FMAs.
-template <class E> struct DownCoef;
-template <> struct DownCoef<EBf16> {
-  bf16x2_t lo, hi;  // (h, 0) and (0, h)
-  __device__ __forceinline__ explicit DownCoef(float h) {
-    const uint32_t b = f32_to_bf16_bits(h);
-    lo = __builtin_bit_cast(bf16x2_t, b);
-    hi = __builtin_bit_cast(bf16x2_t, b << 16);
-  }
-  __device__ __forceinline__ void axpy(const u32x4_t& w, float* y) const {
-    const bf16x8_t wh = __builtin_bit_cast(bf16x8_t, w);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x2_t pr{wh[2 * i], wh[2 * i + 1]};
-      y[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(pr, lo, y[2 * i], false);
-      y[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, hi, y[2 * i + 1], false);
-    }
-  }
-};
-template <> struct DownCoef<EF32> {
-  float h;
-  __device__ __forceinline__ explicit DownCoef(float v) : h(v) {}
-  __device__ __forceinline__ void axpy(const u32x4_t& w, float* y) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = fmaf(h, __uint_as_float(w[i]), y[i]);
-  }
-};
 
 // Inclusive prefix sum over the wave (Hillis-Steele with shuffles); small and
 // only run once per 64 tiles.
@@ -268,7 +232,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
       for (int q = 0; q < kU; ++q) hq[q] = aa[q] * wave_sum(hq[q]);
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        const DownCoef<E> hc(hq[q]);
+        const AxpyCoef<E> hc(hq[q]);
 #pragma unroll
         for (int v = 0; v < NV; ++v) hc.axpy(wd[q][v], yf[v]);
       }
@@ -470,7 +434,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
 #pragma unroll
         for (int k = 0; k < TPW; ++k) {
           if (kk[q] == k) {  // wave-uniform
-            const DownCoef<E> hc(hq[q]);
+            const AxpyCoef<E> hc(hq[q]);
 #pragma unroll
             for (int v = 0; v < NV; ++v) hc.axpy(wd[q][v], yf[k][v]);
           }
@@ -588,7 +552,7 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
       }
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        const DownCoef<E> hc(hq[q]);
+        const AxpyCoef<E> hc(hq[q]);
 #pragma unroll
         for (int v = 0; v < NV; ++v) hc.axpy(wd[q][v], yf[v]);
       }
