@@ -35,6 +35,26 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 64 lanes, returned as a wave-uniform value.  Butterflies inside
+// each row of 16 lanes leave every lane with its row's sum; the gfx9 row
+// broadcasts then carry row 0 into row 1 and row 2 into row 3 (row_bcast:15),
+// and row 1 into rows 2 and 3 (row_bcast:31), so lane 63 holds the total: no
+// LDS round trip (a cross-row shuffle goes through ds_bpermute).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);  // row_half_mirror: combine the two quads of each 8
+  v = dpp_add<0x140>(v);  // row_mirror: combine the two 8-lane halves of each row of 16
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // y += c * w over one 16-byte piece of a row held in storage form, y in fp32.

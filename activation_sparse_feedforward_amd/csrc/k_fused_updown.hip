@@ -29,21 +29,6 @@ constexpr int kListCap = 1024;  // list entries per wave and per chunk of tiles
 // gather latency, without spilling at the widest rows.
 template <int NV> constexpr int neurons_in_flight() { return NV <= 1 ? 8 : (NV <= 4 ? 4 : 2); }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the 64 lanes; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_add<0x141>(v);  // row_half_mirror: combine the two quads of each 8
-  v = dpp_add<0x140>(v);  // row_mirror: combine the two 8-lane halves of each row of 16
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
 
 template <class E> struct Vec;  // 16 bytes of storage as fp32 values
 template <> struct Vec<EBf16> {
