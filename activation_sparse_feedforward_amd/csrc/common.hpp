@@ -55,6 +55,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// v of the lane that DPP control CTRL names, 0 where that lane is outside
+// the row (row shifts) or the row is masked off.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_take(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes; every lane must be active.  Shifts
+// by 1, 2, 4 and 8 lanes inside each row of 16 build the row-local sums, then
+// the row broadcasts add row 0's total into row 1 and row 2's into row 3, and
+// rows 0-1's total into rows 2 and 3.  No LDS round trip.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_take<0x111>(v);       // row_shr:1
+  v += dpp_take<0x112>(v);       // row_shr:2
+  v += dpp_take<0x114>(v);       // row_shr:4
+  v += dpp_take<0x118>(v);       // row_shr:8
+  v += dpp_take<0x142, 0xa>(v);  // row_bcast:15
+  v += dpp_take<0x143, 0xc>(v);  // row_bcast:31
+  return v;
+}
+
+// Lane 63's value (an inclusive scan's total) as a wave-uniform value.
+__device__ __forceinline__ int wave_last(int v) { return __builtin_amdgcn_readlane(v, 63); }
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // y += c * w over one 16-byte piece of a row held in storage form, y in fp32.

@@ -58,15 +58,6 @@ __device__ __forceinline__ int wave_max(int v) {
   for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 template <class E> struct VecB;
 template <> struct VecB<EBf16> {
   static constexpr int N = 8;
@@ -196,7 +187,7 @@ __global__ __launch_bounds__(1024) void bwd_nscan_kernel(BwdArgs p) {
   for (int base = 0; base < p.F; base += 1024) {
     const int j = base + threadIdx.x;
     const int v = j < p.F ? p.neuron_off[j] : 0;
-    const int incl = wave_incl_scan(v, lane);
+    const int incl = wave_incl_scan(v);
     if (lane == 63) wpre[wave] = incl;
     __syncthreads();
     int off = carry_s;
@@ -379,8 +370,8 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_ell_dx_kernel(BwdArg
     const int b = b0 + lane;
     int cnt = 0;
     if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
-    const int incl = wave_incl_scan(cnt, lane);
-    const int total = __shfl(incl, 63);
+    const int incl = wave_incl_scan(cnt);
+    const int total = wave_last(incl);
     const int off = incl - cnt;
     if (cnt > 0) {
       const int64_t rec = (t * n_t + b) * C;
@@ -519,8 +510,8 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
       const int cnt = max(0, min(pf_cnt, 16));
       const u32x4_t ix = pf_idx;
       const int spos = (my_tok * n_t + b) * 16;
-      const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kDxList);
+      const int incl = wave_incl_scan(cnt);
+      total = min(wave_last(incl), kDxList);
       const int off = incl - cnt;
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) {
@@ -533,8 +524,8 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
     } else {
       int cnt = 0;
       if (my_act && b < n_t) cnt = max(0, min(p.count[static_cast<int64_t>(my_tok) * n_t + b], C));
-      const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kDxList);
+      const int incl = wave_incl_scan(cnt);
+      total = min(wave_last(incl), kDxList);
       const int off = incl - cnt;
       if (cnt > 0) {
         const int rec = (my_tok * n_t + b) * C;

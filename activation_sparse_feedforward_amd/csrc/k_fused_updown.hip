@@ -100,17 +100,6 @@ __device__ __forceinline__ void lane_dot_piece(const u32x4_t& w, const u32x4_t& 
   }
 }
 
-// Inclusive prefix sum over the wave (Hillis-Steele with shuffles); small and
-// only run once per 64 tiles.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 }  // namespace
 
 // NV = 16-byte vectors per lane per row: d_model = NV * 64 * Vec<E>::N.
@@ -166,8 +155,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
     // counts are clamped to [0, C] and tile-local indices masked to the tile
     // width (a power of two), so even a corrupted TwELL stays in bounds
     if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
-    const int incl = wave_incl_scan(cnt, lane);
-    const int total = __shfl(incl, 63);
+    const int incl = wave_incl_scan(cnt);
+    const int total = wave_last(incl);
     const int off = incl - cnt;
     if (cnt > 0) {
       const int64_t rec = (t * n_t + b) * C;
@@ -338,8 +327,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       const int cnt = max(0, min(pf_cnt, 16));
       const u32x4_t ix = pf_idx;
       const int vpos = (my_tok * n_t + b) * 16;
-      const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kSyncList);
+      const int incl = wave_incl_scan(cnt);
+      total = min(wave_last(incl), kSyncList);
       const int off = incl - cnt;
 #pragma unroll
       for (int s2 = 0; s2 < 16; ++s2) {
@@ -352,8 +341,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     } else {
       int cnt = 0;
       if (my_act && b < n_t) cnt = max(0, min(p.count[static_cast<int64_t>(my_tok) * n_t + b], C));
-      const int incl = wave_incl_scan(cnt, lane);
-      total = min(__shfl(incl, 63), kSyncList);
+      const int incl = wave_incl_scan(cnt);
+      total = min(wave_last(incl), kSyncList);
       const int off = incl - cnt;
       if (cnt > 0) {
         const int64_t rec = (static_cast<int64_t>(my_tok) * n_t + b) * C;
@@ -487,8 +476,8 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
     const int b = b0 + lane;
     int cnt = 0;
     if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
-    const int incl = wave_incl_scan(cnt, lane);
-    const int total = min(__shfl(incl, 63), kTokList);
+    const int incl = wave_incl_scan(cnt);
+    const int total = min(wave_last(incl), kTokList);
     const int off = incl - cnt;
     if (cnt > 0) {
       const int64_t rec = (t * n_t + b) * C;
