@@ -47,7 +47,7 @@ namespace twell {
 namespace {
 
 constexpr int kBlkRows = 64;         // ELL rows per counting-sort block
-constexpr int kNeuronChunk = 8192;   // neurons per LDS mask table (64 KB)
+constexpr int kNeuronChunk = 2048;   // neurons per LDS mask table (16 KB); a multiple of every tile width
 constexpr int kTokWaves = 4;
 constexpr int kTokListCap = 512;
 
@@ -119,25 +119,31 @@ __device__ __forceinline__ float row_dot(const u32x4_t* w, const u32x4_t* x) {
 // block's count for j.
 __global__ __launch_bounds__(256) void bwd_mask_kernel(BwdArgs p) {
   __shared__ unsigned long long mask[kNeuronChunk];
+  __shared__ int64_t rows[kBlkRows];
   const int blk = blockIdx.x;
   const int j0 = blockIdx.y * kNeuronChunk;
   const int nj = min(kNeuronChunk, p.F - j0);
   for (int j = threadIdx.x; j < nj; j += 256) mask[j] = 0ull;
+  const int64_t n_ell = n_ell_of(p);
+  const int64_t i0 = static_cast<int64_t>(blk) * kBlkRows;
+  if (threadIdx.x < kBlkRows) rows[threadIdx.x] = i0 + threadIdx.x < n_ell ? p.ell_rows[i0 + threadIdx.x] : -1;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_t = p.F / p.tile_n;
-  const int64_t n_ell = n_ell_of(p);
-  for (int r = wave; r < kBlkRows; r += 4) {
-    const int64_t i = static_cast<int64_t>(blk) * kBlkRows + r;
-    if (i >= n_ell) break;
-    const int64_t t = p.ell_rows[i];
-    for (int b = lane; b < n_t; b += 64) {
-      const int cnt = max(0, min(p.count[t * n_t + b], p.C));
-      const int64_t rec = (t * n_t + b) * p.C;
-      for (int s = 0; s < cnt; ++s) {
-        const int j = b * p.tile_n + (p.idx[rec + s] & (p.tile_n - 1)) - j0;
-        if (j >= 0 && j < nj) atomicOr(&mask[j], 1ull << r);
-      }
+  // only this chunk's tiles; a wave's 16 rows x those tiles are spread over its
+  // lanes, so each lane walks a few (row, tile) items instead of 16 rows
+  const int b0 = j0 / p.tile_n, nb = nj / p.tile_n;
+  constexpr int kRowsPerWave = kBlkRows / 4;
+  for (int it = lane; it < kRowsPerWave * nb; it += 64) {
+    const int r = wave * kRowsPerWave + it / nb;
+    const int b = b0 + it % nb;
+    const int64_t t = rows[r];
+    if (t < 0) continue;
+    const int cnt = max(0, min(p.count[t * n_t + b], p.C));
+    const int64_t rec = (t * n_t + b) * p.C;
+    for (int s = 0; s < cnt; ++s) {
+      const int j = b * p.tile_n + (p.idx[rec + s] & (p.tile_n - 1)) - j0;
+      if (j >= 0 && j < nj) atomicOr(&mask[j], 1ull << r);
     }
   }
   __syncthreads();
