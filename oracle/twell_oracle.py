@@ -243,13 +243,21 @@ def gate_error_bound(x, w_gate_t, dtype: str, rows=None) -> np.ndarray:
     """Elementwise bound on |a_kernel - ReLU(g)| for a kernel that accumulates
     g in float32 over d_model terms (any order) and stores ReLU(g) in ``dtype``.
 
-    Standard float32 summation bound: |fl(sum) - sum| <= K * 2^-24 * sum|x_k w_k|
-    (first order), plus the storage rounding: half an ulp of the stored value,
-    at most 2^-8 |g| for bf16 and 2^-24 |g| for fp32.  ReLU is 1-Lipschitz, so
-    the bound carries through it.
+    Accumulation: with S = sum_k |x_k w_k|, each of the K roundings of a
+    float32 dot product (the products, then the running sums) moves the result
+    by at most one float32 ulp, i.e. 2^-23 relative, which covers a matrix
+    unit that rounds to nearest as well as one that truncates; to first order
+        |g_kernel - g| <= acc = K * 2^-23 * S   (times 1.01 for the higher terms).
+    Storage: rounding g_kernel to bf16 (nearest, ties to even) moves it by at
+    most half a bf16 ulp, 2^-8 |g_kernel| <= 2^-8 (|g| + acc); float32 storage
+    keeps the accumulator (2^-24 is used).  ReLU is 1-Lipschitz, so
+        |a_kernel - ReLU(g)| <= acc + rel * (|g| + acc).
     """
     x = _f64(x) if rows is None else _f64(x)[rows]
+    w = _f64(w_gate_t)
     K = x.shape[1]
-    s = np.abs(x) @ np.abs(_f64(w_gate_t)).T
+    s = np.abs(x) @ np.abs(w).T
+    g = np.abs(x @ w.T)
+    acc = (K * 2.0 ** -23) * s * 1.01
     rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -24
-    return (K * 2.0 ** -24) * s * 1.01 + rel * (s + 1e-30)
+    return acc + rel * (g + acc) + 1e-30

@@ -350,16 +350,76 @@ def test_backward_active_mask_override_matches_default():
 
 
 # ----------------------------------------------------------------------------- error model
+def _gate_case(T=96, d=2048, F=1024, seed=3):
+    """Inputs shaped and distributed like the 2B-class bench workload (bf16,
+    column-0 density offset), drawn by the shared generator."""
+    from activation_sparse_feedforward_amd import workloads as W
+    inp = W.make_inputs(W.workload(3, T=T, d_model=d, d_ff=F, rho=0.02))
+    return inp["x"].astype(np.float32), inp["w_gate_t"].astype(np.float32)
+
+
+def _f32_gate(x, w, order, truncate=False):
+    """A float32 gate the way a kernel could compute it: products exact
+    (bf16 x bf16 fits float32), running sums rounded to float32 after every
+    term, in the given K order; ``truncate`` rounds toward zero instead of to
+    nearest.  Returns ReLU(g) rounded to bf16 (float64 values)."""
+    acc = np.zeros((x.shape[0], w.shape[0]), np.float32)
+    for k in order:
+        exact = acc.astype(np.float64) + x[:, k:k + 1].astype(np.float64) * w[None, :, k].astype(np.float64)
+        r = exact.astype(np.float32)
+        if truncate:
+            over = np.abs(r.astype(np.float64)) > np.abs(exact)
+            r = np.where(over, np.nextafter(r, np.float32(0)), r)
+        acc = r
+    return O.round_to_storage(np.where(acc > 0, acc, 0).astype(np.float64), "bf16")
+
+
 def test_gate_error_bound_holds_for_float32_accumulation():
-    """The bound used by parity tests covers a float32, any-order accumulation
-    followed by bf16 rounding (simulated here in NumPy float32, reversed order)."""
-    rng = np.random.default_rng(20)
-    T, d, F = 16, 512, 64
-    x = O.round_to_storage(rng.standard_normal((T, d)), "bf16").astype(np.float32)
-    w = O.round_to_storage(rng.standard_normal((F, d)) / math.sqrt(d), "bf16").astype(np.float32)
-    acc = np.zeros((T, F), np.float32)
-    for k in reversed(range(d)):
-        acc = (acc + x[:, k:k + 1] * w[None, :, k]).astype(np.float32)
-    a_kernel = O.round_to_storage(np.where(acc > 0, acc, 0).astype(np.float64), "bf16")
-    a_ref = O.ffn_forward(x, w, w, np.zeros((F, d)))["a"]
-    assert np.all(np.abs(a_kernel - a_ref) <= O.gate_error_bound(x, w, "bf16"))
+    """The bound covers a float32 accumulation in any order, rounded to nearest
+    or truncated, followed by bf16 rounding of ReLU(g)."""
+    x, w = _gate_case(T=32, d=1024, F=256)
+    a_ref = O.ffn_forward(x, w, w, np.zeros(w.shape))["a"]
+    bound = O.gate_error_bound(x, w, "bf16")
+    d = x.shape[1]
+    perm = np.random.default_rng(5).permutation(d)
+    for order, trunc in ((reversed(range(d)), False), (perm, False), (range(d), True), (perm, True)):
+        a_k = _f32_gate(x, w, list(order), truncate=trunc)
+        assert np.all(np.abs(a_k - a_ref) <= bound)
+
+
+def _outside_frac(a_wrong, a_ref, bound):
+    live = (a_ref != 0) | (a_wrong != 0)
+    assert live.sum() > 200
+    return float(np.mean(np.abs(a_wrong - a_ref)[live] > bound[live]))
+
+
+@pytest.mark.parametrize("k_slice", [1, 13, 31])
+def test_gate_error_bound_rejects_a_dropped_k_slice(k_slice):
+    """A gate GEMM that skips one 64-wide K slice (the main loop's step) must
+    fall outside the bound on at least 90% of the active entries."""
+    x, w = _gate_case()
+    a_ref = O.ffn_forward(x, w, w, np.zeros(w.shape))["a"]
+    keep = np.ones(x.shape[1], bool)
+    keep[64 * k_slice:64 * (k_slice + 1)] = False
+    a_wrong = O.round_to_storage(np.maximum((x[:, keep].astype(np.float64) @ w[:, keep].T.astype(np.float64)), 0),
+                                 "bf16")
+    assert _outside_frac(a_wrong, a_ref, O.gate_error_bound(x, w, "bf16")) >= 0.90
+
+
+def test_gate_error_bound_rejects_transposed_weights():
+    """A gate GEMM that reads W_gate^T transposed (square d_model = d_ff) must
+    fall outside the bound on at least 90% of the active entries."""
+    x, w = _gate_case(d=1024, F=1024)
+    a_ref = O.ffn_forward(x, w, w, np.zeros(w.shape))["a"]
+    a_wrong = O.round_to_storage(np.maximum(x.astype(np.float64) @ w.astype(np.float64), 0), "bf16")
+    assert _outside_frac(a_wrong, a_ref, O.gate_error_bound(x, w, "bf16")) >= 0.90
+
+
+def test_gate_error_bound_storage_term_scales_with_the_value():
+    """The storage term is half a bf16 ulp of the value itself (2^-8 |g|), not of
+    the sum of absolute products: for one exact product the bound reduces to it."""
+    x = np.array([[1.5]], np.float32)
+    w = np.array([[0.75], [-0.75]], np.float32)
+    b = O.gate_error_bound(x, w, "bf16")
+    acc = 1 * 2.0 ** -23 * 1.125 * 1.01
+    np.testing.assert_allclose(b[0], acc + 2.0 ** -8 * (1.125 + acc), rtol=1e-12)
