@@ -52,3 +52,51 @@ def poison_(t: torch.Tensor):
     """Fill an output buffer with a non-zero byte pattern so unwritten entries show up."""
     t.view(torch.uint8).fill_(0xA5)
     return t
+
+
+GUARD = 4096      # canary bytes before and after a guarded buffer (keeps 256-byte alignment)
+CANARY = 0x5A
+
+
+def guarded(shape, dtype, device="cuda"):
+    """An output buffer (poisoned with 0xA5) that sits between two 4 KB canary
+    regions of 0x5A in one allocation, so that a write just before or past its
+    ends shows up in ``check_guards``."""
+    n = 1
+    for s in shape:
+        n *= int(s)
+    nbytes = n * torch.empty(0, dtype=dtype).element_size()
+    raw = torch.full((nbytes + 2 * GUARD,), CANARY, dtype=torch.uint8, device=device)
+    body = raw[GUARD:GUARD + nbytes]
+    body.fill_(0xA5)
+    t = body.view(dtype).view(*shape) if nbytes else torch.empty(shape, dtype=dtype, device=device)
+    t._guard_raw = raw
+    t._guard_n = nbytes
+    return t
+
+
+def check_guards(*tensors):
+    """Assert that the canaries around every guarded buffer are untouched."""
+    for t in tensors:
+        raw = getattr(t, "_guard_raw", None)
+        if raw is None:
+            continue
+        n = t._guard_n
+        head = raw[:GUARD]
+        tail = raw[GUARD + n:]
+        assert bool(torch.all(head == CANARY)), f"write before the start of a buffer of {n} bytes"
+        assert bool(torch.all(tail == CANARY)), f"write past the end of a buffer of {n} bytes"
+
+
+def guarded_act(desc):
+    """TwELL planes in guarded buffers."""
+    return T.Act(guarded((desc.T, desc.n_t), torch.int32),
+                 guarded((desc.T, desc.n_t, desc.slots), torch.uint8),
+                 guarded((desc.T, desc.n_t, desc.slots), desc.torch_dtype))
+
+
+def guarded_route(desc, cap):
+    """Hybrid route arrays in guarded buffers (n_rows zeroed, the rest poisoned)."""
+    r = T.Route(guarded((max(desc.T, 1),), torch.int32), guarded((cap,), torch.int32),
+                guarded((3,), torch.int32), guarded((max(desc.T, 1),), torch.uint8))
+    return r

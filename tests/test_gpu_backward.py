@@ -15,7 +15,7 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import desc_for, dev, host64, poison_, say
+from _helpers import check_guards, desc_for, dev, guarded, host64, poison_, say
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-5, "bf16": 1e-2}
@@ -33,11 +33,12 @@ def run_bwd(w, cap, l1=2e-5, label="", check=True):
     y = torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda")
     ws = torch.empty(T.sizes(desc, cap)["ws_hybrid"], dtype=torch.uint8, device="cuda")
     T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, ws)
-    wsb = poison_(torch.empty(T.sizes(desc, cap)["ws_bwd"], dtype=torch.uint8, device="cuda"))
-    dx = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
-    dws = [poison_(torch.empty((w.d_ff, w.d_model), dtype=torch.float32, device="cuda")) for _ in range(3)]
+    wsb = guarded((T.sizes(desc, cap)["ws_bwd"],), torch.uint8)
+    dx = guarded((w.T, w.d_model), desc.torch_dtype)
+    dws = [guarded((w.d_ff, w.d_model), torch.float32) for _ in range(3)]
     T.twell_ffn_bwd(desc, x, act, route, wg, wu, wd, dy, l1, dx, *dws, wsb)
     torch.cuda.synchronize()
+    check_guards(wsb, dx, *dws)
     out = dict(dx=dx, dws=dws, act=act, route=route, desc=desc, tensors=(x, wg, wu, wd, dy), wsb=wsb, gate=gate)
     if not check:
         return out

@@ -11,7 +11,7 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import desc_for, dev, host64, poison_, say
+from _helpers import check_guards, desc_for, dev, guarded, guarded_act, host64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -36,14 +36,13 @@ def test_classic_equals_epilogue_pack(label, w):
     desc = desc_for(w)
     x = dev(inp["x_raw"], w.dtype)
     wg = dev(inp["w_gate_t_raw"], w.dtype)
-    a1, a2 = T.alloc_act(desc), T.alloc_act(desc)
-    for t in list(a1) + list(a2):
-        poison_(t)
-    gate = poison_(torch.empty((desc.T, desc.d_ff), dtype=desc.torch_dtype, device="cuda"))
+    a1, a2 = guarded_act(desc), guarded_act(desc)
+    gate = guarded((desc.T, desc.d_ff), desc.torch_dtype)
     T.twell_pack(desc, x, wg, a1, gate_dbg=gate)
-    ws = poison_(torch.empty(T.sizes(desc)["ws_pack_classic"], dtype=torch.uint8, device="cuda"))
+    ws = guarded((T.sizes(desc)["ws_pack_classic"],), torch.uint8)
     T.twell_pack_classic(desc, x, wg, a2, ws)
     torch.cuda.synchronize()
+    check_guards(*a1, *a2, gate, ws)
     dense = ws[: desc.T * desc.d_ff * (2 if w.dtype == "bf16" else 4)].view(desc.torch_dtype).view(desc.T, desc.d_ff)
     assert torch.equal(dense.view(torch.int16 if w.dtype == "bf16" else torch.int32),
                        gate.view(torch.int16 if w.dtype == "bf16" else torch.int32))

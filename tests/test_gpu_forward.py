@@ -6,11 +6,13 @@ Checks per case:
     lies within the fp32-accumulation + storage-rounding bound of the oracle's
     float64 ReLU(g);
   * pack: the kernel's TwELL equals, bit for bit, the oracle packer applied to
-    the kernel's own dense gate output; the device stats equal the counts;
+    the kernel's own dense gate output, on every row (also at full size); the
+    device stats equal the counts;
   * fused forward: y within tol * max|y_ref| of the oracle's TwELL forward on
     the kernel's TwELL (tol 1e-5 fp32, 1e-2 bf16), and of the oracle's dense
     FFN wherever no tile overflows;
-  * dense FFN: y within the same tolerance of the oracle's dense FFN.
+  * dense FFN: y within the same tolerance of the oracle's dense FFN;
+  * every output buffer sits between canary regions that must stay untouched.
 """
 import dataclasses
 
@@ -21,7 +23,7 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import desc_for, dev, host64, poison_, say
+from _helpers import check_guards, desc_for, dev, guarded, guarded_act, host64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -33,21 +35,22 @@ def _run_pack_fwd(w, desc, inp, dbg=True):
     wg = dev(inp["w_gate_t_raw"], w.dtype)
     wu = dev(inp["w_up_t_raw"], w.dtype)
     wd = dev(inp["w_down_raw"], w.dtype)
-    act = T.alloc_act(desc)
-    for t in act:
-        poison_(t)
-    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
-    gate = poison_(torch.empty((desc.T, desc.d_ff), dtype=desc.torch_dtype, device="cuda")) if dbg else None
-    y = poison_(torch.empty((desc.T, desc.d_model), dtype=desc.torch_dtype, device="cuda"))
+    act = guarded_act(desc)
+    stats = guarded((2,), torch.int64)
+    stats.zero_()
+    gate = guarded((desc.T, desc.d_ff), desc.torch_dtype) if dbg else None
+    y = guarded((desc.T, desc.d_model), desc.torch_dtype)
     T.twell_pack(desc, x, wg, act, stats=stats, gate_dbg=gate)
     T.twell_ffn_fwd(desc, x, act, wu, wd, y)
     torch.cuda.synchronize()
+    check_guards(*act, stats, y, *([gate] if dbg else []))
     return dict(x=x, wg=wg, wu=wu, wd=wd, act=act, stats=stats, gate=gate, y=y)
 
 
 def _check_case(w, rows=None, label=""):
     """Run pack + fused forward on workload w and check every output against the oracle.
-    rows: host row sample for the float64 checks (None = all rows)."""
+    The TwELL planes are compared byte for byte on every row; rows: host row
+    sample for the float64 checks of the gate and of y (None = all rows)."""
     say(f"[gpu case] {label} {w.name} T={w.T} d={w.d_model} F={w.d_ff} Tn={w.tile_n} C={w.slots} {w.dtype}")
     inp = W.make_inputs(w)
     desc = desc_for(w)
@@ -60,11 +63,12 @@ def _check_case(w, rows=None, label=""):
     y = host64(r["y"])
     sel = np.arange(w.T) if rows is None else np.asarray(rows)
 
-    # pack: bit-exact against the oracle packer on the kernel's own gate output
-    oc, oi, ov = O.twell_pack(gate[sel], w.tile_n, w.slots)
-    np.testing.assert_array_equal(count[sel], oc)
-    np.testing.assert_array_equal(idx[sel], oi)
-    np.testing.assert_array_equal(val[sel], ov)
+    # pack: bit-exact against the oracle packer on the kernel's own gate output, all rows
+    oc, oi, ov = O.twell_pack(gate, w.tile_n, w.slots)
+    np.testing.assert_array_equal(count, oc)
+    np.testing.assert_array_equal(idx, oi)
+    np.testing.assert_array_equal(val, ov)
+    del oc, oi, ov
     assert stats[1] == int(count.astype(np.int64).sum())
     assert stats[0] == int((count > w.slots).sum())
 
@@ -97,6 +101,8 @@ CASES = [
     ("c3 shape T=600", W.workload(3, T=600)),
     ("c5 rho 5% (overflow)", W.workload(5, T=300, rho=0.05)),
     ("c5 rho 0.1%", W.workload(5, T=300, rho=0.001)),
+    ("c5 rho 1%", W.workload(5, T=300, rho=0.01)),
+    ("c5 rho 2%", W.workload(5, T=300, rho=0.02)),
     ("c5 T=16", W.workload(5, T=16)),
     ("T=1", W.workload(2, T=1)),
     ("c4 lognormal tail", W.workload(4, T=520)),
@@ -172,10 +178,11 @@ def test_dense_ffn(label, w):
     inp = W.make_inputs(w)
     desc = desc_for(w)
     x, wg, wu, wd = (dev(inp[k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
-    y = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
-    ws = torch.empty(T.sizes(desc)["ws_dense_fwd"], dtype=torch.uint8, device="cuda")
+    y = guarded((w.T, w.d_model), desc.torch_dtype)
+    ws = guarded((T.sizes(desc)["ws_dense_fwd"],), torch.uint8)
     T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, y, ws)
     torch.cuda.synchronize()
+    check_guards(y, ws)
     yr = O.ffn_forward(inp["x"], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])["y"]
     err = np.abs(host64(y) - yr).max()
     assert err <= TOL[w.dtype] * np.abs(yr).max(), (err, np.abs(yr).max())
@@ -191,22 +198,25 @@ def _sample_rows(T_, seed=0, n_rand=192):
 
 @pytest.mark.parametrize("cfg", [2, 3])
 def test_full_size_sampled_rows(cfg):
-    """Full workload sizes, the launch configuration the benchmark times;
-    float64 checks on sampled rows (first and last M tiles plus random rows)."""
+    """Full workload sizes, the launch configuration the benchmark times: TwELL
+    byte for byte on all rows, float64 checks of the gate and y on sampled rows
+    (the first and last 256 rows plus 192 random ones)."""
     w = W.workload(cfg)
     r, _ = _check_case(w, rows=_sample_rows(w.T, cfg), label=f"full c{cfg}")
     # two generations of lockstep workgroups at c3: a second call gives the same bits
-    y2 = poison_(torch.empty_like(r["y"]))
+    y2 = guarded(tuple(r["y"].shape), r["y"].dtype)
     T.twell_ffn_fwd(desc_for(w), r["x"], r["act"], r["wu"], r["wd"], y2)
     torch.cuda.synchronize()
+    check_guards(y2)
     assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
 
 
 def test_lockstep_three_generations_sampled():
     """24 608 tokens (d_model = 512): 769 lockstep workgroups of 32 rows, i.e.
-    three generations on 256 CUs and a ragged fourth of one workgroup, so the
-    start barrier of every later generation and its rotation shift run; rows
-    around each generation boundary are checked."""
+    three launches of one generation each on 256 CUs and a ragged fourth of one
+    workgroup, so the per-generation launch offsets and the rotation shift of
+    every later generation run; rows around each generation boundary are
+    checked."""
     w = W.workload(3, T=24608, d_model=512)
     rows = set(_sample_rows(w.T, 11).tolist())
     for b in (8192, 16384, 24576):
@@ -222,10 +232,11 @@ def test_dense_ffn_full_size_sampled():
     inp = W.make_inputs(w)
     desc = desc_for(w)
     x, wg, wu, wd = (dev(inp[k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
-    y = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
-    ws = torch.empty(T.sizes(desc)["ws_dense_fwd"], dtype=torch.uint8, device="cuda")
+    y = guarded((w.T, w.d_model), desc.torch_dtype)
+    ws = guarded((T.sizes(desc)["ws_dense_fwd"],), torch.uint8)
     T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, y, ws)
     torch.cuda.synchronize()
+    check_guards(y, ws)
     rows = _sample_rows(w.T, 7)
     yr = O.ffn_forward(inp["x"][rows], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])["y"]
     err = np.abs(host64(y)[rows] - yr).max()

@@ -5,7 +5,8 @@ fallback rows) against the CPU oracle, through the C ABI.
     applied to the kernel's own counts (with the dense-row cap applied);
   * y: ELL rows within tol of the oracle's TwELL forward on the kernel's
     TwELL; dense rows within tol of the oracle's dense FFN; and every row
-    within tol of the dense FFN when no row exceeds the cap.
+    within tol of the dense FFN when no row exceeds the cap;
+  * the canaries around every output buffer and the workspace stay untouched.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import desc_for, dev, host64, poison_, say
+from _helpers import check_guards, desc_for, dev, guarded, guarded_act, guarded_route, host64, poison_, say
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-5, "bf16": 1e-2}
@@ -25,15 +26,14 @@ def run_hybrid(w, cap, rows=None, label=""):
     inp = W.make_inputs(w)
     desc = desc_for(w)
     x, wg, wu, wd = (dev(inp[k + "_raw"], w.dtype) for k in ("x", "w_gate_t", "w_up_t", "w_down"))
-    act = T.alloc_act(desc)
+    act = guarded_act(desc)
     T.twell_pack(desc, x, wg, act)
-    route = T.alloc_route(desc, cap)
-    for t in route:
-        poison_(t)
-    ws = torch.empty(T.sizes(desc, cap)["ws_hybrid"], dtype=torch.uint8, device="cuda")
-    y = poison_(torch.empty((w.T, w.d_model), dtype=desc.torch_dtype, device="cuda"))
+    route = guarded_route(desc, cap)
+    ws = guarded((T.sizes(desc, cap)["ws_hybrid"],), torch.uint8)
+    y = guarded((w.T, w.d_model), desc.torch_dtype)
     T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, ws)
     torch.cuda.synchronize()
+    check_guards(*act, *route, ws, y)
 
     count = act.count.cpu().numpy()
     idx = act.idx.cpu().numpy()
