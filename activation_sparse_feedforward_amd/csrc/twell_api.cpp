@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "../../include/twell.h"
+#include "api_internal.hpp"
 #include "internal.hpp"
 
 namespace {
@@ -157,6 +158,111 @@ int lockstep_resident() {
 
 }  // namespace twell
 
+namespace twell {
+
+twell_status hybrid_check(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                          const void* w_up_t, const void* w_down, void* y, const twell_route* route,
+                          size_t* ws_need) {
+  TWELL_TRY(check_desc(d));
+  if (!route || route->max_dense_rows < 0 || !ws_need) return TWELL_EINVAL;
+  *ws_need = 0;
+  if (d->T == 0) return TWELL_OK;
+  TWELL_TRY(check_dense_ptr(x));
+  TWELL_TRY(check_dense_ptr(w_gate_t));
+  TWELL_TRY(check_act(act));
+  TWELL_TRY(check_dense_ptr(w_up_t));
+  TWELL_TRY(check_dense_ptr(w_down));
+  TWELL_TRY(check_dense_ptr(y));
+  if (!route->ell_rows || !route->n_rows || !route->row_kind) return TWELL_EINVAL;
+  if (route->max_dense_rows > 0 && !route->dense_rows) return TWELL_EINVAL;
+  if (!aligned4(route->ell_rows) || !aligned4(route->n_rows) ||
+      (route->dense_rows && !aligned4(route->dense_rows)))
+    return TWELL_EINVAL;
+  *ws_need = hybrid_ws(d, route->max_dense_rows).total;
+  return TWELL_OK;
+}
+
+twell_status hybrid_launch(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
+                           const void* w_up_t, const void* w_down, void* y, const twell_route* route,
+                           void* ws, void* stream) {
+  const HybridWs hw = hybrid_ws(d, route->max_dense_rows);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(ws);
+
+  twell::RouteArgs r{};
+  r.count = act.count;
+  r.T = d->T;
+  r.n_t = d->d_ff / d->tile_n;
+  r.C = d->slots;
+  r.cap = route->max_dense_rows;
+  r.flags = route->row_kind;
+  r.block_dense = reinterpret_cast<int32_t*>(wsb + hw.block_dense);
+  r.ell_rows = route->ell_rows;
+  r.dense_rows = route->dense_rows;
+  r.n_rows = route->n_rows;
+  r.row_total = reinterpret_cast<int32_t*>(wsb + hw.row_total);
+  r.block_total = reinterpret_cast<int32_t*>(wsb + hw.block_total);
+  r.light_rows = reinterpret_cast<int32_t*>(wsb + hw.light);
+  r.heavy_rows = reinterpret_cast<int32_t*>(wsb + hw.heavy);
+  r.split_n = reinterpret_cast<int32_t*>(wsb + hw.split_n);
+  r.block_heavy = reinterpret_cast<int32_t*>(wsb + hw.block_heavy);
+  r.heavy_cap = heavy_cap(d);
+  TWELL_TRY(from_hip(twell::launch_route(r, s)));
+  TWELL_TRY(from_hip(twell::launch_route_split(r, s)));
+
+  twell::FusedArgs f{};
+  f.x = x;
+  f.count = act.count;
+  f.idx = act.idx;
+  f.val = act.val;
+  f.w_up_t = w_up_t;
+  f.w_down = w_down;
+  f.y = y;
+  f.rows = r.light_rows;
+  f.n_rows_dev = r.split_n + 0;
+  f.T = d->T;
+  f.d = d->d_model;
+  f.F = d->d_ff;
+  f.tile_n = d->tile_n;
+  f.C = d->slots;
+  TWELL_TRY(from_hip(twell::launch_fused_updown(f, d->dtype, s)));
+  twell::FusedArgs fh = f;  // heavy ELL rows, cut into tile ranges
+  fh.rows = r.heavy_rows;
+  fh.n_rows_dev = r.split_n + 1;
+  fh.groups = heavy_groups(d);
+  fh.part = reinterpret_cast<float*>(wsb + hw.heavy_part);
+  fh.part_rows = r.heavy_cap;
+  TWELL_TRY(from_hip(twell::launch_fused_split(fh, d->dtype, s)));
+
+  if (route->max_dense_rows == 0) return TWELL_OK;
+  twell::GateUpArgs g{};
+  g.x = x;
+  g.w_gate_t = w_gate_t;
+  g.w_up_t = w_up_t;
+  g.h = wsb + hw.h;
+  g.rows = route->dense_rows;
+  g.n_rows_dev = route->n_rows + 1;
+  g.M = route->max_dense_rows;
+  g.d = d->d_model;
+  g.F = d->d_ff;
+  TWELL_TRY(from_hip(twell::launch_gateup(g, d->dtype, s)));
+  twell::DownArgs dn{};
+  dn.h = wsb + hw.h;
+  dn.w_down = w_down;
+  dn.y = y;
+  dn.rows = route->dense_rows;
+  dn.n_rows_dev = route->n_rows + 1;
+  dn.M = route->max_dense_rows;
+  dn.d = d->d_model;
+  dn.F = d->d_ff;
+  dn.splits = dense_splits(d);
+  dn.part = reinterpret_cast<float*>(wsb + hw.part);
+  return from_hip(twell::launch_down(dn, d->dtype, s));
+}
+
+
+}  // namespace twell
+
 extern "C" {
 
 twell_status twell_sizes(const twell_desc* d, int64_t max_dense_rows, twell_sizes_t* out) {
@@ -233,94 +339,11 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
 twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
                                   const void* w_up_t, const void* w_down, void* y, const twell_route* route,
                                   void* ws, size_t ws_bytes, void* stream) {
-  TWELL_TRY(check_desc(d));
-  if (!route || route->max_dense_rows < 0) return TWELL_EINVAL;
+  size_t need = 0;
+  TWELL_TRY(twell::hybrid_check(d, x, w_gate_t, act, w_up_t, w_down, y, route, &need));
   if (d->T == 0) return TWELL_OK;
-  TWELL_TRY(check_dense_ptr(x));
-  TWELL_TRY(check_dense_ptr(w_gate_t));
-  TWELL_TRY(check_act(act));
-  TWELL_TRY(check_dense_ptr(w_up_t));
-  TWELL_TRY(check_dense_ptr(w_down));
-  TWELL_TRY(check_dense_ptr(y));
-  if (!route->ell_rows || !route->n_rows || !route->row_kind) return TWELL_EINVAL;
-  if (route->max_dense_rows > 0 && !route->dense_rows) return TWELL_EINVAL;
-  if (!aligned4(route->ell_rows) || !aligned4(route->n_rows) ||
-      (route->dense_rows && !aligned4(route->dense_rows)))
-    return TWELL_EINVAL;
-  const HybridWs hw = hybrid_ws(d, route->max_dense_rows);
-  if (!ws || !aligned16(ws) || ws_bytes < hw.total) return TWELL_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* wsb = static_cast<char*>(ws);
-
-  twell::RouteArgs r{};
-  r.count = act.count;
-  r.T = d->T;
-  r.n_t = d->d_ff / d->tile_n;
-  r.C = d->slots;
-  r.cap = route->max_dense_rows;
-  r.flags = route->row_kind;
-  r.block_dense = reinterpret_cast<int32_t*>(wsb + hw.block_dense);
-  r.ell_rows = route->ell_rows;
-  r.dense_rows = route->dense_rows;
-  r.n_rows = route->n_rows;
-  r.row_total = reinterpret_cast<int32_t*>(wsb + hw.row_total);
-  r.block_total = reinterpret_cast<int32_t*>(wsb + hw.block_total);
-  r.light_rows = reinterpret_cast<int32_t*>(wsb + hw.light);
-  r.heavy_rows = reinterpret_cast<int32_t*>(wsb + hw.heavy);
-  r.split_n = reinterpret_cast<int32_t*>(wsb + hw.split_n);
-  r.block_heavy = reinterpret_cast<int32_t*>(wsb + hw.block_heavy);
-  r.heavy_cap = heavy_cap(d);
-  TWELL_TRY(from_hip(twell::launch_route(r, s)));
-  TWELL_TRY(from_hip(twell::launch_route_split(r, s)));
-
-  twell::FusedArgs f{};
-  f.x = x;
-  f.count = act.count;
-  f.idx = act.idx;
-  f.val = act.val;
-  f.w_up_t = w_up_t;
-  f.w_down = w_down;
-  f.y = y;
-  f.rows = r.light_rows;
-  f.n_rows_dev = r.split_n + 0;
-  f.T = d->T;
-  f.d = d->d_model;
-  f.F = d->d_ff;
-  f.tile_n = d->tile_n;
-  f.C = d->slots;
-  TWELL_TRY(from_hip(twell::launch_fused_updown(f, d->dtype, s)));
-  twell::FusedArgs fh = f;  // heavy ELL rows, cut into tile ranges
-  fh.rows = r.heavy_rows;
-  fh.n_rows_dev = r.split_n + 1;
-  fh.groups = heavy_groups(d);
-  fh.part = reinterpret_cast<float*>(wsb + hw.heavy_part);
-  fh.part_rows = r.heavy_cap;
-  TWELL_TRY(from_hip(twell::launch_fused_split(fh, d->dtype, s)));
-
-  if (route->max_dense_rows == 0) return TWELL_OK;
-  twell::GateUpArgs g{};
-  g.x = x;
-  g.w_gate_t = w_gate_t;
-  g.w_up_t = w_up_t;
-  g.h = wsb + hw.h;
-  g.rows = route->dense_rows;
-  g.n_rows_dev = route->n_rows + 1;
-  g.M = route->max_dense_rows;
-  g.d = d->d_model;
-  g.F = d->d_ff;
-  TWELL_TRY(from_hip(twell::launch_gateup(g, d->dtype, s)));
-  twell::DownArgs dn{};
-  dn.h = wsb + hw.h;
-  dn.w_down = w_down;
-  dn.y = y;
-  dn.rows = route->dense_rows;
-  dn.n_rows_dev = route->n_rows + 1;
-  dn.M = route->max_dense_rows;
-  dn.d = d->d_model;
-  dn.F = d->d_ff;
-  dn.splits = dense_splits(d);
-  dn.part = reinterpret_cast<float*>(wsb + hw.part);
-  return from_hip(twell::launch_down(dn, d->dtype, s));
+  if (!ws || !aligned16(ws) || ws_bytes < need) return TWELL_EINVAL;
+  return twell::hybrid_launch(d, x, w_gate_t, act, w_up_t, w_down, y, route, ws, stream);
 }
 
 twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, const twell_route* route,
@@ -466,6 +489,7 @@ const char* twell_status_str(twell_status s) {
     case TWELL_EINVAL: return "invalid argument (descriptor, pointer, alignment or workspace size)";
     case TWELL_EUNSUPPORTED: return "shape or dtype not supported by the library";
     case TWELL_EHIP: return "HIP launch error";
+    case TWELL_ESCRATCH: return "the problem needs more scratch than the allocation-free entry point holds";
   }
   return "unknown status";
 }

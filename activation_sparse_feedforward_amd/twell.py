@@ -19,11 +19,12 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtwell.so")
 
-TWELL_OK, TWELL_EINVAL, TWELL_EUNSUPPORTED, TWELL_EHIP = 0, 1, 2, 3
+TWELL_OK, TWELL_EINVAL, TWELL_EUNSUPPORTED, TWELL_EHIP, TWELL_ESCRATCH = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 128 << 20  # TWELL_NOALLOC_SCRATCH_BYTES
 TWELL_FP32, TWELL_BF16 = 0, 1
 
 EXPORTED = ("twell_sizes", "twell_pack", "twell_pack_classic", "twell_ffn_fwd", "twell_ffn_fwd_hybrid",
-            "twell_ffn_bwd", "twell_dense_ffn_fwd", "twell_status_str")
+            "twell_ffn_bwd", "twell_dense_ffn_fwd", "twell_status_str", "twell_ffn_fwd_hybrid_noalloc")
 
 
 class TwellError(RuntimeError):
@@ -69,6 +70,7 @@ def library() -> ctypes.CDLL:
         sig = {
             "twell_sizes": (ST, [D, I64, ctypes.POINTER(CSizes)]),
             "twell_ffn_fwd_hybrid": (ST, [D, P, P, CAct, P, P, P, R, P, SZ, P]),
+            "twell_ffn_fwd_hybrid_noalloc": (ST, [D, P, P, CAct, P, P, P, R, P]),
             "twell_ffn_bwd": (ST, [D, P, CAct, R, P, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]),
             "twell_pack": (ST, [D, P, P, CAct, P, P, P]),
             "twell_pack_classic": (ST, [D, P, P, CAct, P, SZ, P]),
@@ -244,6 +246,22 @@ def twell_ffn_fwd_hybrid(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_down, y, r
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
         _ptr(y, "y", desc.T * desc.d_model * e, dt), ctypes.byref(cr), _ptr(ws, "ws", need),
         ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
+
+
+def twell_ffn_fwd_hybrid_noalloc(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_down, y, route: Route,
+                                 stream=None):
+    """twell_ffn_fwd_hybrid with the library's static device scratch as its
+    workspace: allocates nothing (see include/twell.h for the size limit and
+    the rule that calls on one device must not overlap)."""
+    e = 2 if desc.dtype == "bf16" else 4
+    dt = desc.torch_dtype
+    cr = _route(desc, route)
+    _check("twell_ffn_fwd_hybrid_noalloc", library().twell_ffn_fwd_hybrid_noalloc(
+        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
+        _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
+        _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
+        _ptr(y, "y", desc.T * desc.d_model * e, dt), ctypes.byref(cr), _stream(stream)))
 
 
 def twell_ffn_bwd(desc: Desc, x, act: Act, route: Route, w_gate_t, w_up_t, w_down, dy, l1_coef: float,

@@ -30,22 +30,26 @@
  *    others hold idx 0 and value +0.  A value is a non-zero iff its rounded
  *    (stored) value is not zero.
  *  - Pointers: every array argument is a DEVICE pointer, 16-byte aligned,
- *    owned by the caller.  The library never allocates or frees memory and
- *    keeps no state between calls; scratch memory is passed in as `ws`.
+ *    owned by the caller.  The library never allocates or frees memory;
+ *    scratch memory is passed in as `ws`, except by the allocation-free
+ *    twell_ffn_fwd_hybrid_noalloc, whose scratch is a static device array.
  *  - Streams: `stream` is a hipStream_t passed as void* (NULL = default
  *    stream).  All calls are asynchronous: they return after host-side
  *    validation and the kernel launches, with no host synchronisation.
  *  - Errors: TWELL_EINVAL for a bad descriptor, NULL / misaligned pointer or
  *    too-small workspace (nothing is launched); TWELL_EUNSUPPORTED for a valid
- *    shape the library has no kernel for; TWELL_EHIP when a launch fails.
+ *    shape the library has no kernel for; TWELL_EHIP when a launch fails;
+ *    TWELL_ESCRATCH when a problem exceeds the allocation-free entry point's
+ *    static scratch (nothing is launched).
  *    Data-dependent conditions (overflowing tiles, dense-row cap exceeded) are
  *    reported in device counters, never as host errors.
  *  - Supported shapes: dtype BF16 with d_model % 512 == 0 and d_model <= 4096,
  *    or FP32 with d_model % 256 == 0 and d_model <= 2048; tile_n in {64, 128};
  *    d_ff % tile_n == 0; 1 <= slots <= tile_n; T >= 0 (T == 0 is a no-op);
  *    T * max(d_model, d_ff) < 2^31.
- *  - Threading: calls are thread-safe (the only shared state is a per-device
- *    cache of the CU count, held in atomics).
+ *  - Threading: calls are thread-safe (the shared state is a per-device cache
+ *    of the CU count and of the scratch address, held in atomics), except that
+ *    calls of twell_ffn_fwd_hybrid_noalloc must not overlap on one device.
  */
 #ifndef TWELL_H
 #define TWELL_H
@@ -61,7 +65,8 @@ typedef enum {
   TWELL_OK = 0,
   TWELL_EINVAL = 1,
   TWELL_EUNSUPPORTED = 2,
-  TWELL_EHIP = 3
+  TWELL_EHIP = 3,
+  TWELL_ESCRATCH = 4 /* the problem needs more scratch than the allocation-free entry point holds */
 } twell_status;
 
 typedef enum { TWELL_FP32 = 0, TWELL_BF16 = 1 } twell_dtype;
@@ -191,6 +196,29 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
                            const void* w_gate_t, const void* w_up_t, const void* w_down, const void* dy,
                            float l1_coef, void* dx, float* dw_gate_t, float* dw_up_t, float* dw_down,
                            void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the static device scratch array of twell_ffn_fwd_hybrid_noalloc
+ * (one copy per device the library runs on, held until the process ends). */
+#define TWELL_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* twell_ffn_fwd_hybrid without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels, results (bit for
+ * bit) and route outputs as twell_ffn_fwd_hybrid; its workspace is instead a
+ * static device array of TWELL_NOALLOC_SCRATCH_BYTES per device, whose device
+ * address is looked up (hipGetSymbolAddress) on the first call on each
+ * device.  It calls no hipMalloc / hipFree and allocates nothing.
+ *   Limit: twell_sizes(d, route->max_dense_rows).ws_hybrid must not exceed
+ *   TWELL_NOALLOC_SCRATCH_BYTES, else TWELL_ESCRATCH is returned and nothing
+ *   is launched (e.g. the 2B-class shape, T = 16384, d_model = 2048,
+ *   d_ff = 8192, fits with max_dense_rows up to 454).
+ *   Every call on a device shares that device's array: calls that overlap on
+ *   one device (other streams, other threads) race and must not be issued.
+ *   The array keeps the last call's contents; no part of it needs to start
+ *   at zero (every workspace entry is written before it is read). */
+twell_status twell_ffn_fwd_hybrid_noalloc(const twell_desc* d, const void* x, const void* w_gate_t,
+                                          twell_act act, const void* w_up_t, const void* w_down, void* y,
+                                          const twell_route* route, void* stream);
 
 /* The library's own dense MFMA FFN, the baseline the sparse path is compared with.
  * [P2 §Problema: GPUs are built for dense matrix products; the sparse path must

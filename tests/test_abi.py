@@ -84,6 +84,28 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.twell_ffn_fwd_hybrid(ctypes.byref(d), P, P, act, P, P, P, ctypes.byref(r0), P, 1 << 30, None) == T.TWELL_EINVAL
 
 
+def test_noalloc_host_checks_before_any_hip_call():
+    """The allocation-free hybrid forward validates like the workspace entry
+    point, and refuses a problem whose workspace exceeds its static scratch
+    (TWELL_ESCRATCH) before any HIP call."""
+    lib = T.library()
+    act = T.CAct(0x1000, 0x2000, 0x3000)
+    P = 0x10000
+    big = T.Desc(16384, 2048, 8192, 128, 16, "bf16")
+    assert T.sizes(big, 1024)["ws_hybrid"] > T.NOALLOC_SCRATCH_BYTES
+    r = T.CRoute(P, P, P, P, 1024)
+    f = lib.twell_ffn_fwd_hybrid_noalloc
+    assert f(ctypes.byref(big.c()), P, P, act, P, P, P, ctypes.byref(r), None) == T.TWELL_ESCRATCH
+    assert f(ctypes.byref(big.c()), P, P, act, P, P, P, None, None) == T.TWELL_EINVAL
+    assert f(ctypes.byref(big.c()), P, P + 2, act, P, P, P, ctypes.byref(r), None) == T.TWELL_EINVAL
+    assert f(None, P, P, act, P, P, P, ctypes.byref(r), None) == T.TWELL_EINVAL
+    r0 = T.CRoute(P, 0, P, P, 10)  # capacity without a dense_rows array
+    assert f(ctypes.byref(big.c()), P, P, act, P, P, P, ctypes.byref(r0), None) == T.TWELL_EINVAL
+    e = T.Desc(0, 2048, 8192, 128, 16, "bf16")
+    assert f(ctypes.byref(e.c()), None, None, T.CAct(0, 0, 0), None, None, None, ctypes.byref(r), None) == T.TWELL_OK
+    assert "scratch" in T.status_str(T.TWELL_ESCRATCH)
+
+
 def test_empty_batch_is_a_noop():
     lib = T.library()
     d = T.Desc(0, 512, 1024, 128, 16, "bf16").c()
@@ -95,7 +117,7 @@ def test_empty_batch_is_a_noop():
 
 
 def test_status_strings():
-    for c in range(4):
+    for c in range(5):
         assert T.status_str(c)
     assert "unknown" in T.status_str(99)
 
