@@ -1,4 +1,5 @@
-// Fused TwELL up + down projection, one dispatch.
+// Fused TwELL up + down projection: one fused kernel (the lockstep variant is
+// dispatched once per generation of resident workgroups, on disjoint rows).
 //
 // Follows the TwELL page ("Sakana AI and NVIDIA introduce TwELL with CUDA
 // kernels...", section "¿Qué hace distinto a TwELL frente a ELL clásico?"):

@@ -6,11 +6,13 @@
 // activation columns are cut into tiles equal to the matmul's N tile, and the
 // non-zeros are packed locally per tile.  Here every wave owns complete rows
 // of one TwELL tile in its MFMA accumulators, so each (row, tile) is compacted
-// straight from registers: a wavefront ballot per 32-column block gives the
-// non-zero mask of two rows at once, and popcounts of the masks give every
-// non-zero its slot in ascending column order -- no atomics and no dense
-// store of ReLU(g); the compact records are assembled in LDS and leave with
-// wide stores.
+// on chip: a wavefront ballot per 32-column block gives the non-zero mask of
+// two rows at once, and the masks give every non-zero its slot in ascending
+// column order -- no atomics and no dense store of ReLU(g); the compact
+// records leave with wide stores.  bf16 with 16 slots (the 2B-class format)
+// stages the rounded rows in LDS and lets each lane pack one row
+// (pack_epilogue_rows); other formats compact straight from the accumulator
+// registers (pack_epilogue_lc, pack_epilogue).
 //
 // T_n = 128 uses the 256 x 256 direct-to-LDS core (gemm256.hpp); T_n = 64 the
 // 256 x 64 register-staged core (gemm_core.hpp); batches of at most 64 tokens
@@ -311,6 +313,133 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
   }
 }
 
+// Row-staged variant for bf16 and C = 16, for a wave tile of 128 rows x one
+// TwELL tile of 128 columns whose B operand was loaded in natural order (lane
+// l of accumulator block j holds tile column 32 j + l).  The wave's rows are
+// handled in two halves of 64:
+//  1. per accumulator register (two rows x 32 columns per block), ReLU(g) is
+//     rounded to bf16 with the packed conversion (round to nearest even) and
+//     written to this wave's LDS scratch as row-major rows; one ballot per
+//     32-column block is the non-zero mask of those columns of the two rows,
+//     in ascending column order, and lane i collects (v_writelane) the four
+//     mask words of row i;
+//  2. lane i then owns row i: its count is the popcount of its mask, and it
+//     takes its first C non-zeros in ascending column order by repeatedly
+//     clearing the lowest set bit, reading each value back from the row in
+//     LDS and placing index and value into a 48-byte record held in registers,
+//     which leaves with three 16-byte stores.
+// A stored value is non-zero iff the fp32 bits are >= 0x8001 (signed), so the
+// masks come from the raw accumulator bits; only masked positions are read
+// back, hence the ReLU clamp is applied only for the debug copy of the rows.
+// There are no per-register branches and no cross-lane slot arithmetic.
+// wlds: kRowsScratch bytes, 16-byte aligned.
+constexpr int kRowStride = 272;                      // 256 B of values + 16 B so rows start on different banks
+constexpr int kRowsScratch = 64 * kRowStride;        // one half (64 rows) per wave
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
+}
+
+template <bool DBG>
+__device__ __forceinline__ void pack_epilogue_rows(const PackArgs& p, const f32x16_t (&acc)[4][4], int64_t wrow0,
+                                                   int b, char* wlds, uint32_t& ovf, uint32_t& nnz) {
+  constexpr int C = 16;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, li = lane & 31;
+  const int n_t = p.F / 128;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    uint32_t mk[4] = {0u, 0u, 0u, 0u};  // lane i: non-zero mask of row i of this half, columns 32 w ..
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const int mb = 2 * hb + m2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ra = m2 * 32 + 8 * (r >> 2) + (r & 3);  // row of lanes 0-31 in the half; lanes 32-63: ra + 4
+        int u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u[j] = __float_as_int(acc[mb][j][r]);
+          if constexpr (DBG) u[j] = max(u[j], 0);
+        }
+        uint16_t* rowp = reinterpret_cast<uint16_t*>(wlds + (ra + 4 * half) * kRowStride);
+        const uint32_t p01 = cvt_pk_bf16(__int_as_float(u[0]), __int_as_float(u[1]));
+        const uint32_t p23 = cvt_pk_bf16(__int_as_float(u[2]), __int_as_float(u[3]));
+        rowp[li] = static_cast<uint16_t>(p01);
+        rowp[32 + li] = static_cast<uint16_t>(p01 >> 16);
+        rowp[64 + li] = static_cast<uint16_t>(p23);
+        rowp[96 + li] = static_cast<uint16_t>(p23 >> 16);
+        uint64_t m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = __builtin_amdgcn_ballot_w64(u[j] >= 0x8001);
+        // lane ra takes row ra's mask words, lane ra + 4 those of row ra + 4.
+        // A VALU read of an SGPR that a VALU compare has just written needs two
+        // wait states, which the compiler cannot insert inside the asm.
+        asm("s_nop 1\n\t"
+            "v_writelane_b32 %0, %4, %12\n\tv_writelane_b32 %0, %5, %13\n\t"
+            "v_writelane_b32 %1, %6, %12\n\tv_writelane_b32 %1, %7, %13\n\t"
+            "v_writelane_b32 %2, %8, %12\n\tv_writelane_b32 %2, %9, %13\n\t"
+            "v_writelane_b32 %3, %10, %12\n\tv_writelane_b32 %3, %11, %13"
+            : "+v"(mk[0]), "+v"(mk[1]), "+v"(mk[2]), "+v"(mk[3])
+            : "s"(static_cast<uint32_t>(m[0])), "s"(static_cast<uint32_t>(m[0] >> 32)),
+              "s"(static_cast<uint32_t>(m[1])), "s"(static_cast<uint32_t>(m[1] >> 32)),
+              "s"(static_cast<uint32_t>(m[2])), "s"(static_cast<uint32_t>(m[2] >> 32)),
+              "s"(static_cast<uint32_t>(m[3])), "s"(static_cast<uint32_t>(m[3] >> 32)), "i"(ra), "i"(ra + 4));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t row = wrow0 + hb * 64 + lane;
+    const bool row_ok = row < p.T;
+    const uint16_t* myrow = reinterpret_cast<const uint16_t*>(wlds + lane * kRowStride);
+    if constexpr (DBG) {
+      if (row_ok) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(myrow);
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.gate_dbg) + (row * p.F + b * 128) * 2);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) dst[c] = src[c];
+      }
+    }
+    const int cnt = __builtin_popcount(mk[0]) + __builtin_popcount(mk[1]) + __builtin_popcount(mk[2]) +
+                    __builtin_popcount(mk[3]);
+    uint32_t ri[4] = {0u, 0u, 0u, 0u};                  // C index bytes
+    uint32_t rv[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // C bf16 values
+#pragma unroll
+    for (int s = 0; s < C; ++s) {
+      if (__builtin_amdgcn_ballot_w64(s < cnt) == 0) break;  // uniform: no row has another non-zero
+      if (s < cnt) {
+        const bool z0 = mk[0] == 0u, z1 = mk[1] == 0u, z2 = mk[2] == 0u;
+        const uint32_t w = !z0 ? mk[0] : (!z1 ? mk[1] : (!z2 ? mk[2] : mk[3]));
+        const int col = (!z0 ? 0 : (!z1 ? 32 : (!z2 ? 64 : 96))) + __builtin_ctz(w);
+        const uint32_t wc = w & (w - 1u);
+        if (!z0) mk[0] = wc;
+        else if (!z1) mk[1] = wc;
+        else if (!z2) mk[2] = wc;
+        else mk[3] = wc;
+        ri[s >> 2] |= static_cast<uint32_t>(col) << (8 * (s & 3));
+        rv[s >> 1] |= static_cast<uint32_t>(myrow[col]) << (16 * (s & 1));
+      }
+    }
+    if (row_ok) {
+      const int64_t rt = row * n_t + b;
+      p.count[rt] = cnt;
+      *reinterpret_cast<u32x4_t*>(p.idx + rt * C) = u32x4_t{ri[0], ri[1], ri[2], ri[3]};
+      u32x4_t* vd = reinterpret_cast<u32x4_t*>(static_cast<char*>(p.val) + rt * C * 2);
+      vd[0] = u32x4_t{rv[0], rv[1], rv[2], rv[3]};
+      vd[1] = u32x4_t{rv[4], rv[5], rv[6], rv[7]};
+    }
+    if (p.stats) {
+      const int cv = row_ok ? cnt : 0;
+      ovf += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(cv > C)));
+      nnz += static_cast<uint32_t>(wave_last(wave_incl_scan(cv)));
+    }
+    __builtin_amdgcn_wave_barrier();  // all rows read before the next half overwrites them
+  }
+}
+
 // Bytes of LDS scratch one wave's epilogue needs.
 __host__ __device__ constexpr int pack_scratch_bytes(int C, int eb) { return ((32 * C * (1 + eb)) + 15) & ~15; }
 // The lane-column epilogue adds 64 dummy index bytes and 64 dummy values (one per lane).
@@ -330,6 +459,9 @@ __device__ __forceinline__ void pack_stats(const PackArgs& p, uint32_t ovf, uint
 // [128*(w/2), +128) and TwELL tile 2*nt + (w%2).
 template <class E, bool DBG, int kC>
 __global__ __launch_bounds__(256, 1) void gate_pack256_kernel(PackArgs p) {
+  // bf16 with C = 16 takes the row-staged epilogue (natural column order on
+  // the B operand); other cases the lane-column one
+  constexpr bool kRows = E::kBytes == 2 && kC == 16;
   extern __shared__ __align__(16) char lds[];
   const int n_mt = static_cast<int>((p.T + kT256 - 1) / kT256);
   const int n_nt = (p.F + kT256 - 1) / kT256;
@@ -339,15 +471,19 @@ __global__ __launch_bounds__(256, 1) void gate_pack256_kernel(PackArgs p) {
   const int64_t n0 = static_cast<int64_t>(nt) * kT256;
   DirectRows<E> la, lb;
   la.init(p.x, p.d, m0, p.T, nullptr);
-  lb.init(p.w_gate_t, p.d, n0, p.F, nullptr, /*lane_cols=*/true);
+  lb.init(p.w_gate_t, p.d, n0, p.F, nullptr, /*lane_cols=*/!kRows);
   Acc256 acc;
   gemm256_mainloop<E>(la, lb, p.d / (128 / E::kBytes), lds, acc);
   const int wave = threadIdx.x >> 6;
   const int b = static_cast<int>((n0 >> 7) + (wave & 1));
   uint32_t ovf = 0, nnz = 0;
   __syncthreads();  // every wave is done with the operand stages: reuse them as epilogue scratch
-  char* wlds = lds + wave * pack_lc_scratch_bytes(kC > 0 ? kC : p.C, E::kBytes);
-  if (b < p.F / 128) pack_epilogue_lc<E, DBG, kC>(p, acc.c, m0 + (wave >> 1) * 128, b, wlds, ovf, nnz);
+  if constexpr (kRows) {
+    if (b < p.F / 128) pack_epilogue_rows<DBG>(p, acc.c, m0 + (wave >> 1) * 128, b, lds + wave * kRowsScratch, ovf, nnz);
+  } else {
+    char* wlds = lds + wave * pack_lc_scratch_bytes(kC > 0 ? kC : p.C, E::kBytes);
+    if (b < p.F / 128) pack_epilogue_lc<E, DBG, kC>(p, acc.c, m0 + (wave >> 1) * 128, b, wlds, ovf, nnz);
+  }
   pack_stats(p, ovf, nnz);
 }
 
@@ -386,6 +522,7 @@ template <class E, bool DBG>
 static hipError_t launch_pack256_t(const PackArgs& a, hipStream_t s) {
   // 4 waves' epilogue scratch must fit in the operand stages it reuses
   static_assert(4 * pack_lc_scratch_bytes(128, 4) <= kLds256, "pack scratch exceeds the GEMM stages");
+  static_assert(4 * kRowsScratch <= kLds256, "row scratch exceeds the GEMM stages");
   return a.C == 16 ? launch_pack256_c<E, DBG, 16>(a, s) : launch_pack256_c<E, DBG, 0>(a, s);
 }
 

@@ -140,14 +140,22 @@ twell_status twell_pack(const twell_desc* d, const void* x, const void* w_gate_t
 twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,
                                 void* ws, size_t ws_bytes, void* stream);
 
-/* Fused up + down projection on TwELL input, in ONE fused kernel.
+/* Fused up + down projection on TwELL input: one fused kernel, the
+ * intermediate never written to memory.
  * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down
  * projections together; the intermediate never reaches global memory.]
- * Batches of 2048 rows and more take the lockstep kernel, launched once per
- * generation of workgroups the device runs at once (one per CU, 32 rows each:
- * two launches at 16384 rows on 256 CUs) on disjoint row blocks, so each
- * generation starts together; every row is still computed start to finish by
- * one workgroup of one launch.
+ * Dispatches: rows wider than 2048 elements (bf16; 1024 in fp32) take a
+ * one-wave-per-row kernel and batches below 2048 rows a one-workgroup-per-row
+ * kernel, each in ONE dispatch.  Batches of 2048 rows and more take the lockstep kernel
+ * (32-row workgroups that sweep the neuron tiles together), dispatched once
+ * per generation of workgroups the device runs at once (one per CU), on
+ * disjoint row blocks: ceil(ceil(T / 32) / CUs) dispatches of the same
+ * kernel, e.g. 2 at T = 16384 on a 256-CU MI355X.  Every row is computed
+ * start to finish by one workgroup of one dispatch.
+ * Bits: each row's tiles are summed starting at a chunk that depends on its
+ * workgroup's index and generation, hence on the device's CU count; y is
+ * bitwise reproducible on one device (and on devices with the same CU count),
+ * and within the stated tolerance elsewhere.
  * For every row t and stored slot (neuron j = b*tile_n + idx, value a):
  *   u = x[t] . w_up_t[j];  h = a * u;  y[t] += h * w_down[j]   (fp32 accumulate)
  * y [T x d_model] is overwritten (stored in dtype).  A tile with count > slots
@@ -191,7 +199,10 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
  * row the forward served lossily from TwELL is differentiated the same way);
  * rows in route->dense_rows are recomputed densely on MFMA.
  * Deterministic: the weight gradients of each neuron are summed in ascending
- * token order.  ws: twell_sizes(d, route->max_dense_rows).ws_bwd bytes. */
+ * token order (bitwise the same on any device).  dx of the ELL rows comes from
+ * a lockstep kernel dispatched once per generation of resident workgroups like
+ * twell_ffn_fwd's, with the same dependence of its bits on the CU count.
+ * ws: twell_sizes(d, route->max_dense_rows).ws_bwd bytes. */
 twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, const twell_route* route,
                            const void* w_gate_t, const void* w_up_t, const void* w_down, const void* dy,
                            float l1_coef, void* dx, float* dw_gate_t, float* dw_up_t, float* dw_down,
