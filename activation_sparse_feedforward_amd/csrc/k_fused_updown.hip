@@ -606,13 +606,20 @@ static hipError_t launch_sync_cfg(const FusedArgs& args, hipStream_t s) {
 
 // Tokens per wave: as many fp32 y rows as fit beside the loads in 128 VGPRs,
 // and no more than the per-chunk list holds when one tile of each token is
-// full (TPW * C <= kSyncList, so every chunk of >= 1 tile fits).
+// full (TPW * C <= kSyncList, so every chunk of >= 1 tile fits), but fewer when
+// that would leave CUs without a workgroup (e.g. 8192 rows at d_model = 1024:
+// 4 tokens per wave give 128 workgroups for 256 CUs, 2 give 256).
 template <class E, int NV>
 static hipError_t launch_sync_t(const FusedArgs& a, hipStream_t s) {
   constexpr int kMax = NV * Vec<E>::N <= 16 ? 4 : 2;
   const int fit = kSyncList / a.C;
-  if (kMax >= 4 && fit >= 4) return launch_sync_cfg<E, NV, 4, 1>(a, s);
-  if (fit >= 2) return launch_sync_cfg<E, NV, 2, 1>(a, s);
+  const int64_t cus = lockstep_resident();
+  auto fills = [&](int tpw) {
+    const int64_t per = static_cast<int64_t>(kSyncWaves) * tpw;
+    return cus <= 0 || (a.T + per - 1) / per >= cus;
+  };
+  if (kMax >= 4 && fit >= 4 && fills(4)) return launch_sync_cfg<E, NV, 4, 1>(a, s);
+  if (fit >= 2 && fills(2)) return launch_sync_cfg<E, NV, 2, 1>(a, s);
   return launch_sync_cfg<E, NV, 1, 1>(a, s);
 }
 

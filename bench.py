@@ -60,6 +60,10 @@ def parse():
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --calib-copy-mib run into profiles/traffic_<kernel>.json")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --traffic-summary")
+    ap.add_argument("--gather-ceiling", action="store_true",
+                    help="instead of the step line: the gather-ceiling probe alone (rows of the 2B-class "
+                         "W_up^T / W_down, random and XCD-shared, two and eight rows in flight per wave); "
+                         "prints one JSON line")
     return ap.parse_args()
 
 
@@ -145,8 +149,11 @@ def traffic_summary(fetch_csv: str, write_csv: str, calib_mib: int, command: str
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(inp, budget_s: float):
-    """Time the CPU oracle's dense float64 forward on a bounded token sample."""
+def cpu_baseline(inp, budget_s: float, tile_n: int, slots: int, dtype: str):
+    """Time the CPU oracle on bounded token samples of the timed workload: its
+    dense float64 forward, and its sparse path (float64 gate, ReLU rounded to
+    the storage dtype, TwELL pack, TwELL forward), each for about half the
+    budget."""
     import numpy as np
     from oracle import twell_oracle as O
     try:
@@ -156,16 +163,77 @@ def cpu_baseline(inp, budget_s: float):
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     x = inp["x"]
     chunk = 256
-    done, t0 = 0, time.perf_counter()
-    while done < x.shape[0]:
-        O.ffn_forward(x[done:done + chunk], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])
-        done += chunk
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} tokens of the timed workload, oracle dense float64 forward "
-                      f"(NumPy matmul), {dt:.1f} s"}
+
+    def run(fn, budget):
+        done, t0 = 0, time.perf_counter()
+        while done < x.shape[0]:
+            fn(x[done:done + chunk])
+            done += chunk
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, time.perf_counter() - t0
+
+    def sparse(xs):
+        _, a = O.gate_forward(xs, inp["w_gate_t"])
+        c, i, v = O.twell_pack(O.round_to_storage(a, dtype), tile_n, slots)
+        return O.twell_forward(xs, c, i, v, tile_n, inp["w_up_t"], inp["w_down"])
+
+    nd, td = run(lambda xs: O.ffn_forward(xs, inp["w_gate_t"], inp["w_up_t"], inp["w_down"]), budget_s / 2)
+    ns, ts = run(sparse, budget_s / 2)
+    return {"value": nd / td, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"dense: first {nd} tokens of the timed workload, oracle float64 forward (NumPy matmul), "
+                      f"{td:.1f} s; sparse path: first {ns} tokens, oracle gate + TwELL pack + TwELL forward, "
+                      f"{ts:.1f} s",
+            "sparse_path_value": ns / ts}
+
+
+def gather_ceiling(wu, wd, stream, steps=256, reps=5):
+    """Rate at which the memory system serves the fused kernel's access pattern
+    (16 waves per CU, whole weight rows, two rows per step) with no arithmetic:
+    random rows (mostly past L2) and rows shared by every wave of an XCD
+    (mostly from L2), each with two and with eight rows in flight per wave.
+    Returns GB/s per case and the ceilings (best of the two depths)."""
+    import ctypes
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "activation_sparse_feedforward_amd", "libtwell_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the library first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.twell_probe_gather.restype = ctypes.c_int
+    lib.twell_probe_gather.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, P, P]
+    rows, row_bytes = wu.shape[0], wu.shape[1] * wu.element_size()
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 16, dtype=torch.int32, device="cuda")
+    st = stream.cuda_stream
+
+    def run(shared, depth):
+        rc = lib.twell_probe_gather(wu.data_ptr(), wd.data_ptr(), rows, row_bytes, steps, shared, depth, blocks,
+                                    out.data_ptr(), st)
+        if rc != 0:
+            raise RuntimeError(f"twell_probe_gather returned {rc}")
+
+    res = {}
+    for shared, name in ((0, "random"), (1, "xcd_shared")):
+        for depth in (1, 4):
+            run(shared, depth)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(shared, depth)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            nbytes = blocks * 16 * steps * 2 * row_bytes
+            res[f"{name}_rows_{2 * depth}_in_flight_gbs"] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    res["random_ceiling_gbs"] = max(res["random_rows_2_in_flight_gbs"], res["random_rows_8_in_flight_gbs"])
+    res["xcd_shared_ceiling_gbs"] = max(res["xcd_shared_rows_2_in_flight_gbs"], res["xcd_shared_rows_8_in_flight_gbs"])
+    res["bytes_per_launch"] = blocks * 16 * steps * 2 * row_bytes
+    return res
 
 
 def _pct(v):
@@ -219,6 +287,26 @@ def hipblaslt_dense(x, wg, wu, wd, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def step_bounds(w, density):
+    """Lower bounds in microseconds on one MI355X (8 TB/s HBM, 2.5 PFLOP/s bf16
+    MFMA) for the gate+pack kernel (read x and W_gate once, or its MFMA work),
+    the fused kernel (its strictly required bytes: x, TwELL, every touched
+    weight row once, y) and the dense FFN (read x and the three weights, write
+    and read h, write y; or its MFMA work)."""
+    eb = 2 if w.dtype == "bf16" else 4
+    n_t = w.d_ff // w.tile_n
+    xb = w.T * w.d_model * eb
+    wb = w.d_ff * w.d_model * eb
+    twell = w.T * n_t * (4 + w.slots * (1 + eb))
+    touched = 1.0 - (1.0 - density) ** w.T
+    gate = max((xb + wb + twell) / (PEAK_HBM_GBS * 1e3), 2.0 * w.T * w.d_model * w.d_ff / (PEAK_BF16_TFLOPS * 1e6))
+    fused = (2 * xb + twell + 2 * touched * wb) / (PEAK_HBM_GBS * 1e3)
+    dense = max((2 * xb + 3 * wb + 2 * w.T * w.d_ff * eb) / (PEAK_HBM_GBS * 1e3),
+                6.0 * w.T * w.d_model * w.d_ff / (PEAK_BF16_TFLOPS * 1e6))
+    return {"gate_pack": round(gate, 2), "fused": round(fused, 2), "twell_step": round(gate + fused, 2),
+            "dense": round(dense, 2)}
+
+
 def density_sweep(T, W, args):
     """TwELL forward (pack + fused, and pack + hybrid) against the library's
     dense FFN over the sweep densities at the 2B-class shape, plus a 16-token
@@ -270,6 +358,16 @@ def density_sweep(T, W, args):
         hyb_ms = timed(lambda: T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, wsh, stream=stream))
         dense_ms = timed(lambda: T.twell_dense_ffn_fwd(desc, x, wg, wu, wd, y, wsd, stream=stream))
         gathered = nnz * 2 * w.d_model * 2
+        bnd = step_bounds(w, nnz / (w.T * w.d_ff))
+        extra = {"bounds_us": bnd,
+                 "gate_pack_frac_of_bound": round(bnd["gate_pack"] / (pack_ms * 1e3), 4),
+                 "fused_frac_of_bound": round(bnd["fused"] / (fused_ms * 1e3), 4),
+                 "dense_frac_of_bound": round(bnd["dense"] / (dense_ms * 1e3), 4),
+                 "speedup_plain_vs_dense_bound": round(bnd["dense"] / ((pack_ms + fused_ms) * 1e3), 3)}
+        if w.T <= 64 and not args.no_hipblaslt:
+            tm = hipblaslt_dense(x, wg, wu, wd, args.steps, args.warmup, stream)
+            extra["dense_torch_matmul_ms"] = round(tm, 4)
+            extra["speedup_plain_vs_torch_matmul"] = round(tm / (pack_ms + fused_ms), 3)
         out.append({"rho_target": rho, "T": w.T, "measured_density": round(nnz / (w.T * w.d_ff), 6),
                     "overflow_tiles": ovf, "dense_rows": n_rows[1], "dense_over_cap": n_rows[2],
                     "pack_ms": round(pack_ms, 4), "fused_ms": round(fused_ms, 4),
@@ -277,7 +375,8 @@ def density_sweep(T, W, args):
                     "speedup_plain": round(dense_ms / (pack_ms + fused_ms), 3),
                     "speedup_hybrid": round(dense_ms / (pack_ms + hyb_ms), 3),
                     "fused_gathered_gbs": round(gathered / (fused_ms * 1e-3) / 1e9, 1),
-                    "gate_pack_tflops": round(2.0 * w.T * w.d_model * w.d_ff / (pack_ms * 1e-3) / 1e12, 1)})
+                    "gate_pack_tflops": round(2.0 * w.T * w.d_model * w.d_ff / (pack_ms * 1e-3) / 1e12, 1),
+                    **extra})
         print(json.dumps({"sweep_point": out[-1]}), file=sys.stderr, flush=True)
         del x, wg, wu, wd, act, route, wsh, wsd, y
         torch.cuda.empty_cache()
@@ -336,15 +435,29 @@ def train_step(T, W, args, steps, warmup):
     twell_peak = torch.cuda.max_memory_allocated() - base
     # what the forward keeps for the backward: the TwELL planes and the route (x is an input)
     saved = sz["count"] + sz["idx"] + sz["val"] + 4 * (max(w.T, 1) + cap + 3) + max(w.T, 1)
+    ws_bytes = sz["ws_hybrid"] + sz["ws_bwd"]
     out = {"workload": w.name, "ms_per_step": round(tot, 4), "tokens_per_s": round(w.T / tot * 1e3, 1),
            "phases_ms": {"pack": round(ph[0], 4), "hybrid_fwd": round(ph[1], 4), "bwd": round(ph[2], 4)},
            "n_ell": n_rows[0], "n_dense": n_rows[1], "dense_over_cap": n_rows[2],
-           "saved_activation_bytes": int(saved), "workspace_bytes": int(sz["ws_hybrid"] + sz["ws_bwd"]),
+           "saved_activation_bytes": int(saved), "workspace_bytes": int(ws_bytes),
            "step_peak_extra_bytes": int(twell_peak)}
     if not args.no_dense:
-        out["dense_torch_matmul"] = dense_train_torch(x, wg, wu, wd, dy, w.l1_coef, steps, warmup, stream)
-        out["speedup_vs_dense_train"] = round(out["dense_torch_matmul"]["ms_per_step"] / tot, 3)
-        out["saved_activation_ratio"] = round(saved / out["dense_torch_matmul"]["saved_activation_bytes"], 4)
+        dn = dense_train_torch(x, wg, wu, wd, dy, w.l1_coef, steps, warmup, stream)
+        out["dense_torch_matmul"] = dn
+        out["speedup_vs_dense_train"] = round(dn["ms_per_step"] / tot, 3)
+        out["saved_activation_ratio"] = round(saved / dn["saved_activation_bytes"], 4)
+        # device memory a step needs beyond its inputs, weights and outputs, on both sides: TwELL keeps
+        # the planes and the route from forward to backward and uses caller workspaces sized for
+        # max_dense_rows (plus whatever it allocates during the step); the dense step's peak
+        # allocation minus the outputs it allocates itself (y, dx and three bf16 dW)
+        outputs = 2 * w.T * w.d_model * 2 + 3 * w.d_ff * w.d_model * 2
+        twell_mem = saved + ws_bytes + twell_peak
+        dense_mem = dn["step_peak_extra_bytes"] - outputs
+        out["step_memory"] = {"twell_bytes": int(twell_mem), "dense_bytes": int(dense_mem),
+                              "ratio": round(twell_mem / dense_mem, 4),
+                              "twell_parts": {"saved": int(saved), "workspaces": int(ws_bytes),
+                                              "allocated_in_step": int(twell_peak)},
+                              "dense_outputs_excluded": int(outputs), "max_dense_rows": cap}
     return out
 
 
@@ -427,6 +540,13 @@ def main():
         return
     w = W.workload(args.config, T=args.T, rho=args.rho, d_ff=args.d_ff)
     overridden = args.T is not None or args.rho is not None or args.d_ff is not None
+    if args.gather_ceiling:
+        wp = W.make_inputs(w)
+        wu_p, wd_p = (torch.from_numpy(np.ascontiguousarray(wp[k + "_raw"]).view(np.int16)).view(torch.bfloat16).cuda()
+                      for k in ("w_up_t", "w_down"))
+        print(json.dumps({"gather_ceiling": gather_ceiling(wu_p, wd_p, torch.cuda.current_stream()),
+                          "rows": "W_up^T and W_down of " + w.name}), flush=True)
+        return
     wname = w.name if not overridden else f"{w.name}@T{w.T}_F{w.d_ff}_rho{w.rho}"
     inp = W.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -575,6 +695,13 @@ def main():
         fused_past_gbs = past_l2 / (fused_ms * 1e-3) / 1e9
         fused_info.update({"past_l2_bytes": int(past_l2), "past_l2_gbs": round(fused_past_gbs, 1),
                            "past_l2_frac_of_hbm_peak": round(fused_past_gbs / PEAK_HBM_GBS, 4)})
+    # the same rows gathered by the probe: cache-served and past-L2 ceilings of this access pattern
+    if w.dtype == "bf16":
+        ceil = gather_ceiling(wu, wd, stream)
+        fused_info["gather_ceiling"] = ceil
+        fused_info["gathered_frac_of_ceiling"] = round(fused_info["gathered_gbs"] / ceil["xcd_shared_ceiling_gbs"], 4)
+        if past_l2:
+            fused_info["past_l2_frac_of_ceiling"] = round(fused_info["past_l2_gbs"] / ceil["random_ceiling_gbs"], 4)
 
     out = {
         "metric": "TwELL FFN tokens/sec at 99.5% act. sparsity; speedup vs dense; % roofline",
@@ -609,7 +736,7 @@ def main():
         torch.cuda.empty_cache()
         out["training"] = train_step(T, W, args, max(3, K // 2), 2)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, w.tile_n, w.slots, w.dtype)
     print(json.dumps(out), flush=True)
 
 

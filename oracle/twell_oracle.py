@@ -52,7 +52,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "ffn_forward", "round_to_storage", "twell_pack", "twell_unpack", "twell_forward",
+    "gate_forward", "ffn_forward", "round_to_storage", "twell_pack", "twell_unpack", "twell_forward",
     "route", "hybrid_forward", "ffn_backward", "ffn_loss", "gate_error_bound",
 ]
 
@@ -64,6 +64,14 @@ def _f64(a) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Dense forward  [P2 §Receta: ReLU gate in a gated FFN]
 # ---------------------------------------------------------------------------
+def gate_forward(x, w_gate_t):
+    """The gate in float64: g = x W_gate (pre-activation) and a = ReLU(g).
+    The first step of ``ffn_forward`` (and of the sparse path, whose TwELL is
+    the packing of a)."""
+    g = _f64(x) @ _f64(w_gate_t).T
+    return g, np.where(g > 0.0, g, 0.0)
+
+
 def ffn_forward(x, w_gate_t, w_up_t, w_down) -> dict:
     """Plain dense gated FFN in float64.
 
@@ -71,8 +79,7 @@ def ffn_forward(x, w_gate_t, w_up_t, w_down) -> dict:
     Returns all intermediates as float64 arrays.
     """
     x = _f64(x)
-    g = x @ _f64(w_gate_t).T
-    a = np.where(g > 0.0, g, 0.0)
+    g, a = gate_forward(x, w_gate_t)
     u = x @ _f64(w_up_t).T
     h = a * u
     y = h @ _f64(w_down)
