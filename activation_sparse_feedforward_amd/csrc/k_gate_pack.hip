@@ -329,8 +329,10 @@ __device__ __forceinline__ void pack_epilogue_lc(const PackArgs& p, const f32x16
 //     LDS and placing index and value into a 48-byte record held in registers,
 //     which leaves with three 16-byte stores.
 // A stored value is non-zero iff the fp32 bits are >= 0x8001 (signed), so the
-// masks come from the raw accumulator bits; only masked positions are read
-// back, hence the ReLU clamp is applied only for the debug copy of the rows.
+// masks come from the accumulator bits, clamped at 0 (the ReLU) as integers.
+// (Only masked positions are read back, so the clamp matters only for the
+// debug copy of the rows; without it the compiler copies the accumulators out
+// early and spills nine registers per lane, 19 MB of scratch traffic per call.)
 // There are no per-register branches and no cross-lane slot arithmetic.
 // wlds: kRowsScratch bytes, 16-byte aligned.
 constexpr int kRowStride = 272;                      // 256 B of values + 16 B so rows start on different banks
@@ -361,8 +363,7 @@ __device__ __forceinline__ void pack_epilogue_rows(const PackArgs& p, const f32x
         int u[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          u[j] = __float_as_int(acc[mb][j][r]);
-          if constexpr (DBG) u[j] = max(u[j], 0);
+          u[j] = max(__float_as_int(acc[mb][j][r]), 0);
         }
         uint16_t* rowp = reinterpret_cast<uint16_t*>(wlds + (ra + 4 * half) * kRowStride);
         const uint32_t p01 = cvt_pk_bf16(__int_as_float(u[0]), __int_as_float(u[1]));
