@@ -137,6 +137,21 @@ def test_round_bf16_against_bit_rounding():
     np.testing.assert_array_equal(O.round_to_storage(a, "bf16"), expect)
 
 
+def test_round_bf16_hand_worked_cases():
+    # bf16 keeps 8 significant bits, so in [1, 2) the step is 2^-7 and half a step 2^-8
+    cases = [
+        (1 + 2.0 ** -9, 1.0),                          # below half a step: down
+        (1 + 2.0 ** -8, 1.0),                          # tie, 1.0 has an even last bit: stays
+        (1 + 2.0 ** -7 + 2.0 ** -8, 1 + 2.0 ** -6),    # tie, 1 + 2^-7 has an odd last bit: up to even
+        (1 + 2.0 ** -8 + 2.0 ** -12, 1 + 2.0 ** -7),   # above half: up
+        (2 - 2.0 ** -8, 2.0),                          # tie at the top of the binade: carries to 2
+        (3 * 2.0 ** -10 + 2.0 ** -19, 3 * 2.0 ** -10), # binade [2^-9, 2^-8), step 2^-16: below half
+        (0.0, 0.0),
+    ]
+    got = O.round_to_storage(np.array([c[0] for c in cases]), "bf16")
+    np.testing.assert_array_equal(got, [c[1] for c in cases])
+
+
 # ----------------------------------------------------------------------------- forward
 def _brute_ffn(x, wg, wu, wd):
     T, d = x.shape
