@@ -140,8 +140,9 @@ twell_status from_hip(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_
 
 namespace twell {
 
-// One lockstep workgroup per CU (their LDS or VGPR footprint); 0 turns the
-// start barrier off when the device cannot be queried.
+// Workgroups of the lockstep kernels the device runs at once: one per CU
+// (their LDS or VGPR footprint).  0 when the device cannot be queried: the
+// launchers then issue the whole grid in one dispatch.
 int lockstep_resident() {
   static std::atomic<int> cached[64];
   int dev = 0;

@@ -223,7 +223,8 @@ def twell_pack_classic(desc: Desc, x, w_gate_t, act: Act, ws, stream=None):
 
 
 def twell_ffn_fwd(desc: Desc, x, act: Act, w_up_t, w_down, y, stream=None):
-    """Fused TwELL up + down projection in one dispatch (see include/twell.h)."""
+    """Fused TwELL up + down projection: one fused kernel, dispatched once per
+    generation of resident workgroups for large batches (see include/twell.h)."""
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
     _check("twell_ffn_fwd", library().twell_ffn_fwd(

@@ -147,11 +147,15 @@ twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* 
  * Dispatches: rows wider than 2048 elements (bf16; 1024 in fp32) take a
  * one-wave-per-row kernel and batches below 2048 rows a one-workgroup-per-row
  * kernel, each in ONE dispatch.  Batches of 2048 rows and more take the lockstep kernel
- * (32-row workgroups that sweep the neuron tiles together), dispatched once
- * per generation of workgroups the device runs at once (one per CU), on
- * disjoint row blocks: ceil(ceil(T / 32) / CUs) dispatches of the same
- * kernel, e.g. 2 at T = 16384 on a 256-CU MI355X.  Every row is computed
- * start to finish by one workgroup of one dispatch.
+ * (workgroups of 16 waves that sweep the neuron tiles together, each wave
+ * holding R rows: as many as its registers and per-wave list allow -- 2 at
+ * d_model = 2048, 4 at d_model <= 1024 when C <= 32 -- but fewer while that
+ * would leave CUs without a workgroup), dispatched once per generation of
+ * workgroups the device runs at once (one per CU), on disjoint row blocks:
+ * ceil(ceil(T / (16 R)) / CUs) dispatches of the same kernel, e.g. 2 at
+ * T = 16384, d_model = 2048 (R = 2) and 1 at T = 8192, d_model = 1024 (R = 2)
+ * on a 256-CU MI355X.  Every row is computed start to finish by one workgroup
+ * of one dispatch.
  * Bits: each row's tiles are summed starting at a chunk that depends on its
  * workgroup's index and generation, hence on the device's CU count; y is
  * bitwise reproducible on one device (and on devices with the same CU count),
