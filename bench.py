@@ -3,7 +3,8 @@
 
 One step = one pass of the inference hot path over one batch: twell_pack
 (gate GEMM + ReLU + TwELL epilogue, one dispatch) then twell_ffn_fwd (fused
-up + down, one dispatch), on synthetic Llama-2B-shaped FFN inputs already
+up + down: one kernel, dispatched once per generation of resident workgroups,
+two at this shape), on synthetic Llama-2B-shaped FFN inputs already
 resident in HBM (T=16384 tokens, d_model=2048, d_ff=8192, bf16, T_n=128,
 C=16, ~0.5% gate density).  Prints one JSON line.
 
