@@ -538,21 +538,24 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
 // Small batches (T <= 64, bf16, T_n = 128): the work is reading W_gate once, so
 // the tiling is turned around.  One workgroup per TwELL tile (128 neurons),
 // 4 waves of 32 neurons each; the neurons are the MFMA's M side and the tokens
-// its N side (two 32-token blocks).  With only F/128 workgroups, each must keep
-// a lot of its weight stream in flight: 128-byte K slices of the 128 weight
-// rows (16 KB) and of the 64 token rows (8 KB) move global -> LDS with direct
-// loads through a ring of kSmallStages stages, and the wait before using a
-// slice lets the younger stages stay in flight.  ReLU(g), rounded to bf16, is
-// then staged in LDS as [token][128] and each wave packs a quarter of the
-// tokens: lane l holds columns 2l, 2l + 1, and ballots give the slots in
-// ascending column order.  Same stored values and format as the large-batch
-// kernels.
+// its N side (one 32-token block, two above 32 tokens).  With only F/128
+// workgroups, each must keep a lot of its weight stream in flight: 128-byte K
+// slices of the 128 weight rows (16 KB) and of XR token rows (XR = 16, 32 or
+// 64: the batch rounded up) move global -> LDS with direct loads through a
+// ring of NS stages, as many as the LDS holds (8, 7 and 6), and the wait
+// before using a slice lets the younger stages stay in flight.  ReLU(g),
+// rounded to bf16, is then staged in LDS as [token][128] and each wave packs a
+// quarter of the tokens: lane l holds columns 2l, 2l + 1, and ballots give the
+// slots in ascending column order.  Same stored values and format as the
+// large-batch kernels.
 constexpr int kSmallT = 64;
-constexpr int kSmallStages = 6;
-constexpr int kSmallStage = (128 + 64) * 128;                   // W slice + x slice
-constexpr int kSmallLds = kSmallStages * kSmallStage;           // 144 KB; the pack reuses it
 
+template <int XR, int NS>
 __global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
+  constexpr int kStage = (128 + XR) * 128;  // W slice + XR token rows
+  // direct loads of one stage per wave: rows 8 (4q + wave) + lane / 8 for q = 0, 1, ...
+  // up to 128 + XR rows; with XR = 16 waves 2 and 3 issue one fewer
+  constexpr int kLoadsFull = (128 + XR + 31) / 32, kLoadsShort = (128 + XR) / 32;
   extern __shared__ __align__(16) char lds[];
   __shared__ uint32_t ovf_s, nnz_s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -565,48 +568,58 @@ __global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
     nnz_s = 0;
   }
   // direct-load sources: instruction q of wave w fills stage rows 8*(4q + w) + lane/8,
-  // rows 0..127 = weight rows, 128..191 = token rows (clamped to T - 1)
+  // rows 0..127 = weight rows, 128..127 + XR = token rows (clamped to T - 1)
+  // (a fixed-size array: with its size a template constant, captured by the
+  // lambda below, the host pass of hipcc emitted no launch stub for the kernel)
   const char* src[6];
+  static_assert(kLoadsFull <= 6, "load rounds");
 #pragma unroll
-  for (int q = 0; q < 6; ++q) {
-    const int r = 8 * (4 * q + wave) + (lane >> 3);
+  for (int q = 0; q < kLoadsFull; ++q) {
+    const int r = min(8 * (4 * q + wave) + (lane >> 3), 127 + XR);  // (the clamp only feeds unissued loads)
     const int c = (lane & 7) ^ lds_swz(r);
     const char* base = r < 128 ? static_cast<const char*>(p.w_gate_t) +
                                      (static_cast<int64_t>(b) * 128 + r) * p.d * 2
                                : static_cast<const char*>(p.x) + static_cast<int64_t>(min(r - 128, T - 1)) * p.d * 2;
     src[q] = base + c * 16;
   }
+  const bool short_wave = 8 * (4 * kLoadsShort + wave) >= 128 + XR;  // wave-uniform
   auto issue = [&](int kt) {
-    char* st = lds + (kt % kSmallStages) * kSmallStage;
+    char* st = lds + (kt % NS) * kStage;
 #pragma unroll
-    for (int q = 0; q < 6; ++q)
-      __builtin_amdgcn_global_load_lds(src[q] + static_cast<int64_t>(kt) * 128, st + (4 * q + wave) * 8 * 128, 16,
-                                       0, 0);
+    for (int q = 0; q < kLoadsFull; ++q)
+      if (q < kLoadsShort || !short_wave)
+        __builtin_amdgcn_global_load_lds(src[q] + static_cast<int64_t>(kt) * 128, st + (4 * q + wave) * 8 * 128, 16,
+                                         0, 0);
   };
-  const int nk = p.d / 64;  // 128-byte slices; d is a multiple of 512
-  const bool two = T > 32;
+  const int nk = p.d / 64;  // 128-byte slices; d is a multiple of 512, so nk >= 8 >= NS - 1
+  const bool two = XR > 32 && T > 32;
   f32x16_t acc0, acc1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 #pragma unroll
-  for (int q = 0; q < kSmallStages - 1; ++q)
+  for (int q = 0; q < NS - 1; ++q)
     if (q < nk) issue(q);
   for (int kt = 0; kt < nk; ++kt) {
-    // slice kt landed when at most the (kSmallStages - 2) younger slices' loads are outstanding
-    if (kt + kSmallStages - 1 <= nk)
-      asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // 4 x 6 loads
-    else
+    // slice kt landed when at most the (NS - 2) younger slices' loads are outstanding
+    if (kt + NS - 1 <= nk) {
+      if (short_wave)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NS - 2) * kLoadsShort) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NS - 2) * kLoadsFull) : "memory");
+    } else {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    }
     // the stage refilled now was last read in iteration kt - 1, which every
     // wave finished before the barrier above
-    if (kt + kSmallStages - 1 < nk) issue(kt + kSmallStages - 1);
-    const char* st = lds + (kt % kSmallStages) * kSmallStage;
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    const char* st = lds + (kt % NS) * kStage;
     Frag<EBf16> fa[4], fb0[4], fb1[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       read_frag256(fa[kk], st, wave * 32 + li, kk, lane);
-      read_frag256(fb0[kk], st, 128 + li, kk, lane);
-      read_frag256(fb1[kk], st, 160 + li, kk, lane);
+      // tokens past XR (past T) read the last loaded token row: their outputs are discarded
+      read_frag256(fb0[kk], st, 128 + min(li, XR - 1), kk, lane);
+      if constexpr (XR > 32) read_frag256(fb1[kk], st, 160 + li, kk, lane);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -675,12 +688,23 @@ __global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
   }
 }
 
-static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSmallLds);
+template <int XR, int NS>
+static hipError_t launch_pack_small_t(const PackArgs& a, hipStream_t s) {
+  constexpr int lds = NS * (128 + XR) * 128;
+  static_assert(lds >= 64 * 128 * 2, "the pack stages [64][128] bf16 in the ring");
+  static_assert(lds + 64 <= 160 * 1024, "LDS of one workgroup");
+  static_assert(NS - 1 <= 8 && (NS - 2) * ((128 + XR + 31) / 32) <= 63, "prologue depth / vmcnt range");
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel<XR, NS>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(gate_pack_small_kernel, dim3(a.F / 128), dim3(256), kSmallLds, s, a);
+  hipLaunchKernelGGL((gate_pack_small_kernel<XR, NS>), dim3(a.F / 128), dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
+  if (a.T <= 16) return launch_pack_small_t<16, 8>(a, s);
+  if (a.T <= 32) return launch_pack_small_t<32, 7>(a, s);
+  return launch_pack_small_t<64, 6>(a, s);
 }
 
 template <class E>

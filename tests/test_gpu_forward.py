@@ -105,6 +105,10 @@ CASES = [
     ("c5 rho 2%", W.workload(5, T=300, rho=0.02)),
     ("c5 T=16", W.workload(5, T=16)),
     ("T=1", W.workload(2, T=1)),
+    # the small-batch gate kernel stages 16, 32 or 64 token rows by batch size
+    ("small batch T=11", W.workload(3, T=11)),
+    ("small batch T=31", W.workload(3, T=31)),
+    ("small batch T=57 rho 2%", W.workload(5, T=57, rho=0.02)),
     ("c4 lognormal tail", W.workload(4, T=520)),
     ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
     ("wide d_ff=16384", W.workload(4, T=300, d_model=512, d_ff=16384)),
