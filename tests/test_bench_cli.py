@@ -1,5 +1,7 @@
-"""Host-side checks of bench.py (no GPU): the one-GPU refusal and the
-scaling of rocprofv3 byte counters by the calibration copy."""
+"""Host-side checks of bench.py (no GPU): the one-GPU refusal, the scaling of
+rocprofv3 byte counters by the calibration copy, the lower bounds the line
+reports against, and the use of a counter record only for the kernel source it
+was taken on."""
 import csv
 import json
 import os
@@ -64,3 +66,38 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path):
     assert u["calls"] == 2
     assert u["read_bytes_per_launch"] == int(800 * 1024 * 2.0)
     assert u["write_bytes_per_launch"] == int(10 * 1024)
+
+
+def test_step_bounds_closed_forms():
+    """The lower bounds the bench reports against, recomputed from the workload's
+    sizes: MFMA time of the gate GEMM, HBM time of the fused kernel's required
+    bytes (every weight row touched once at 16384 tokens), MFMA time of the
+    dense FFN; at 16 tokens the gate is bound by reading W_gate."""
+    from activation_sparse_feedforward_amd import workloads as W
+    w = W.workload(3)
+    b = bench.step_bounds(w, 0.005)
+    x = 16384 * 2048 * 2
+    wt = 8192 * 2048 * 2
+    twell = 16384 * 64 * (4 + 16 * 3)
+    assert b["gate_pack"] == pytest.approx(2 * 16384 * 2048 * 8192 / 2.5e15 * 1e6, abs=0.01)
+    assert b["fused"] == pytest.approx((2 * x + twell + 2 * wt) / 8e12 * 1e6, abs=0.01)
+    assert b["dense"] == pytest.approx(6 * 16384 * 2048 * 8192 / 2.5e15 * 1e6, abs=0.01)
+    assert b["twell_step"] == pytest.approx(b["gate_pack"] + b["fused"], abs=0.02)
+    s = bench.step_bounds(W.workload(3, T=16), 0.005)
+    touched = 1 - (1 - 0.005) ** 16
+    assert s["gate_pack"] == pytest.approx((16 * 2048 * 2 + wt + 16 * 64 * 52) / 8e12 * 1e6, abs=0.01)
+    assert s["fused"] == pytest.approx((2 * 16 * 2048 * 2 + 16 * 64 * 52 + 2 * touched * wt) / 8e12 * 1e6, abs=0.01)
+    assert s["dense"] == pytest.approx((2 * 16 * 2048 * 2 + 3 * wt + 2 * 16 * 8192 * 2) / 8e12 * 1e6, abs=0.01)
+
+
+def test_measured_traffic_only_for_the_current_kernel_source(tmp_path, monkeypatch):
+    """A committed counter record is used only while the kernel's sources hash
+    the same; otherwise the bench reports no traffic figure."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    h = bench.kernel_source_hash(bench.KERNEL_SOURCES["gate_pack"])
+    (prof / "traffic_gate_pack.json").write_text(json.dumps({"source_hash": h, "bytes_per_launch": 1234}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("gate_pack", h, 1.0) == 1234
+    assert bench.measured_traffic("gate_pack", "0" * 16, 1.0) is None
+    assert bench.measured_traffic("fused_updown", h, 1.0) is None  # no record at all
