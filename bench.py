@@ -61,6 +61,9 @@ def parse():
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --calib-copy-mib run into profiles/traffic_<kernel>.json")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --traffic-summary")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the step line: the MFMA-ceiling probe alone (the gate kernel's occupancy and "
+                         "MFMA instruction with register operands, plus the shader clock during it); prints one JSON line")
     ap.add_argument("--gather-ceiling", action="store_true",
                     help="instead of the step line: the gather-ceiling probe alone (rows of the 2B-class "
                          "W_up^T / W_down, random and XCD-shared, two and eight rows in flight per wave); "
@@ -235,6 +238,60 @@ def gather_ceiling(wu, wd, stream, steps=256, reps=5):
     res["xcd_shared_ceiling_gbs"] = max(res["xcd_shared_rows_2_in_flight_gbs"], res["xcd_shared_rows_8_in_flight_gbs"])
     res["bytes_per_launch"] = blocks * 16 * steps * 2 * row_bytes
     return res
+
+
+def mfma_ceiling(stream, iters=20000, reps=5, random_operands=True):
+    """Rate of the matrix cores under the gate kernel's MFMA load with nothing
+    else: one workgroup of four waves per CU, each wave issuing
+    v_mfma_f32_32x32x16_bf16 on 16 independent accumulators from registers,
+    with operands of random bf16 values (eight A and eight B fragments cycled
+    through, as a GEMM's change every k-step) or one constant fragment pair.
+    Also the shader clock during the loop (shader-clock cycles over 100 MHz
+    ticks, median over the waves) and the cycles one MFMA took at that clock.
+    Returns TFLOP/s (median of `reps` launches) and those figures."""
+    import ctypes
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "activation_sparse_feedforward_amd", "libtwell_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the library first")
+    lib = ctypes.CDLL(path)
+    lib.twell_probe_mfma.restype = ctypes.c_int
+    lib.twell_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    # 16 x 64 pieces of 8 bf16 values, N(0, 1) (finite), seeded
+    g = torch.Generator().manual_seed(5)
+    frags = torch.randn(16 * 64 * 8, generator=g).to(torch.bfloat16).cuda() if random_operands else None
+
+    def run():
+        rc = lib.twell_probe_mfma(iters, blocks, frags.data_ptr() if frags is not None else None, out.data_ptr(),
+                                  clocks.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"twell_probe_mfma returned {rc}")
+
+    run()
+    torch.cuda.synchronize()
+    ts, ghz = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz.append(float(np.median(c[:, 0] / (c[:, 1] / 100e6))) / 1e9)
+    flop = blocks * 4 * iters * 16 * 32768.0
+    ms = float(np.median(ts))
+    clock = float(np.median(ghz))
+    cyc = (float(np.median(clocks.view(-1, 2)[:, 0].cpu().numpy().astype(np.float64)))) / (iters * 16)
+    return {"operands": "random" if random_operands else "constant",
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 1), "clock_ghz": round(clock, 3),
+            "cycles_per_mfma": round(cyc, 2), "peak_at_clock_tflops": round(blocks * 4 * 32768 / 32 * clock * 1e9 / 1e12, 1),
+            "flop_per_launch": flop, "ms_per_launch": round(ms, 4)}
 
 
 def _pct(v):
@@ -541,6 +598,13 @@ def main():
         return
     w = W.workload(args.config, T=args.T, rho=args.rho, d_ff=args.d_ff)
     overridden = args.T is not None or args.rho is not None or args.d_ff is not None
+    if args.mfma_ceiling:
+        st = torch.cuda.current_stream()
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(st),
+                          "mfma_constant_operands": mfma_ceiling(st, random_operands=False),
+                          "kernel": "4 waves per CU, v_mfma_f32_32x32x16_bf16 on 16 accumulators, register operands"}),
+              flush=True)
+        return
     if args.gather_ceiling:
         wp = W.make_inputs(w)
         wu_p, wd_p = (torch.from_numpy(np.ascontiguousarray(wp[k + "_raw"]).view(np.int16)).view(torch.bfloat16).cuda()
@@ -685,6 +749,14 @@ def main():
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                 "traffic": None if overridden or args.config != 3 else measured_traffic("fused_updown", src["fused_updown"], 1)}
 
+    # the gate kernel against what the matrix cores sustain under its MFMA load alone (bf16 only: the
+    # probe issues the bf16 instruction)
+    gate_vs_mfma = None
+    if w.dtype == "bf16":
+        mc = mfma_ceiling(stream)
+        gate_vs_mfma = {"mfma_ceiling": mc, "achieved_tflops": round(gate_flop / (pack_ms * 1e-3) / 1e12, 1),
+                        "frac_of_ceiling": round(gate_flop / (pack_ms * 1e-3) / 1e12 / mc["tflops"], 4)}
+
     # gather phase against the HBM peak: strictly required bytes, and the bytes the kernel moved past
     # L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE of the current source, committed under profiles/)
     fused_req_gbs = fused_bytes / (fused_ms * 1e-3) / 1e9
@@ -724,6 +796,7 @@ def main():
         "overflow_tiles": ovf,
         "phases_ms": {"gate_pack": round(pack_ms, 4), "fused_updown": round(fused_ms, 4)},
         "gate_pack_tflops": round(gate_flop / (pack_ms * 1e-3) / 1e12, 1),
+        "gate_pack_vs_mfma_ceiling": gate_vs_mfma,
         "fused_updown": fused_info,
         "dense_ffn": dense,
         "classic_ell": classic,
