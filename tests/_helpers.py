@@ -3,6 +3,8 @@ reading kernel results back as float64 NumPy arrays.  No arithmetic of the
 method lives here."""
 from __future__ import annotations
 
+import json
+import os
 import re
 import sys
 
@@ -100,3 +102,34 @@ def guarded_route(desc, cap):
     r = T.Route(guarded((max(desc.T, 1),), torch.int32), guarded((cap,), torch.int32),
                 guarded((3,), torch.int32), guarded((max(desc.T, 1),), torch.uint8))
     return r
+
+
+MARGINS_ENV = "TWELL_MARGINS"  # file the GPU parity checks append their error margins to (JSON lines)
+
+
+def within(got, ref, tol: float, label: str, scale=None) -> float:
+    """Assert max|got - ref| <= tol * scale (scale: max|ref| unless given) and
+    report how much of the tolerance was used: printed, and appended as a JSON
+    line to the file named by $TWELL_MARGINS when it is set.  Returns that
+    fraction."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    scale = max(float(np.abs(ref).max()), 1e-30) if scale is None else float(scale)
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    frac = err / (tol * scale)
+    say(f"   [margin] {label}: max|err| = {err / scale:.2e} of max|ref| (tolerance {tol:g}, {100 * frac:.1f}% used)")
+    path = os.environ.get(MARGINS_ENV)
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"label": label, "rel_err": err / scale, "tol": tol, "frac": frac}) + "\n")
+    assert frac <= 1.0, f"{label}: max|err| {err:.3g} > {tol:g} x {scale:.3g}"
+    return frac
+
+
+def record(label: str, rel_err: float):
+    """Report an error figure that is not itself a check (printed, and appended
+    to the $TWELL_MARGINS file when set)."""
+    say(f"   [margin] {label}: {rel_err:.2e} of max|ref|")
+    path = os.environ.get(MARGINS_ENV)
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps({"label": label, "rel_err": rel_err}) + "\n")
