@@ -26,7 +26,8 @@
 //            while the wave walks j's pairs in ascending t, gathering x[t] and
 //            dy[t]; it forms u, dh, dg, du, h for each pair, stores (dg, du)
 //            in the pair's TwELL slot and keeps the three fp32 weight-gradient
-//            rows in VGPRs, written once
+//            rows in VGPRs; at the end it adds the dense rows' part (stored by
+//            the dense-row GEMM, which runs first) and writes each row once
 //   totals   per row, the sum of its counts; the ELL rows are then split into
 //            light rows and at most heavy_cap heavy ones (row total >
 //            max(2 C, 2 x mean)), as in the hybrid forward
@@ -320,14 +321,26 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
   float* og = p.dw_gate_t + j * d;
   float* ou = p.dw_up_t + j * d;
   float* od = p.dw_down + j * d;
+  // the dense rows' GEMM ran first and stored their part of these rows: added
+  // here, once (with no dense rows it wrote nothing, and an empty batch has cap 0
+  // so n_rows is not read)
+  const bool from_dense = p.cap > 0 && p.n_rows[1] > 0;  // uniform
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int64_t c = static_cast<int64_t>(v * kWave + lane) * kN;
 #pragma unroll
     for (int i = 0; i < kN; i += 4) {
-      *reinterpret_cast<f32x4_t*>(og + c + i) = f32x4_t{ag[v][i], ag[v][i + 1], ag[v][i + 2], ag[v][i + 3]};
-      *reinterpret_cast<f32x4_t*>(ou + c + i) = f32x4_t{au[v][i], au[v][i + 1], au[v][i + 2], au[v][i + 3]};
-      *reinterpret_cast<f32x4_t*>(od + c + i) = f32x4_t{ad[v][i], ad[v][i + 1], ad[v][i + 2], ad[v][i + 3]};
+      f32x4_t rg = f32x4_t{ag[v][i], ag[v][i + 1], ag[v][i + 2], ag[v][i + 3]};
+      f32x4_t ru = f32x4_t{au[v][i], au[v][i + 1], au[v][i + 2], au[v][i + 3]};
+      f32x4_t rd = f32x4_t{ad[v][i], ad[v][i + 1], ad[v][i + 2], ad[v][i + 3]};
+      if (from_dense) {
+        rg += *reinterpret_cast<const f32x4_t*>(og + c + i);
+        ru += *reinterpret_cast<const f32x4_t*>(ou + c + i);
+        rd += *reinterpret_cast<const f32x4_t*>(od + c + i);
+      }
+      *reinterpret_cast<f32x4_t*>(og + c + i) = rg;
+      *reinterpret_cast<f32x4_t*>(ou + c + i) = ru;
+      *reinterpret_cast<f32x4_t*>(od + c + i) = rd;
     }
   }
 }

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dx_kernel(BwdArgs p) {
     }
 }
 
-// blockIdx.z: 0 -> dW_gate^T += dG^T x_d, 1 -> dW_up^T += dU^T x_d, 2 -> dW_down += H^T dy_d
+// blockIdx.z: 0 -> dW_gate^T = dG^T x_d, 1 -> dW_up^T = dU^T x_d, 2 -> dW_down = H^T dy_d
+// (stored; the ELL rows' per-neuron pass, launched after this one, adds these
+// rows to its own sums).  With no dense rows nothing is written.
 template <class E>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dw_dense_kernel(BwdArgs p) {
   extern __shared__ __align__(16) char lds[];
@@ -161,8 +163,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dw_dense_kernel(BwdArgs p) {
       if (j >= p.F) continue;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        float* o = out + j * p.d + n0 + nb * 32 + (lane & 31);
-        *o += acc.c[mb][nb][r];
+        out[j * p.d + n0 + nb * 32 + (lane & 31)] = acc.c[mb][nb][r];
       }
     }
 }

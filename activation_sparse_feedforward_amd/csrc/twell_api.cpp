@@ -416,8 +416,11 @@ twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, co
   a.heavy_cap = heavy_cap(d);
   a.groups = heavy_groups(d);
   a.dx_hpart = reinterpret_cast<float*>(wsb + bw.dx_hpart);
-  TWELL_TRY(from_hip(twell::launch_bwd_sparse(a, d->dtype, s)));
-  return from_hip(twell::launch_bwd_dense(a, d->dtype, s));
+  // dense rows first: their weight-gradient GEMM stores its part of dW, which
+  // the ELL rows' per-neuron pass reads and adds to its own sums before its one
+  // write of each row (instead of a separate read-modify-write pass over dW)
+  TWELL_TRY(from_hip(twell::launch_bwd_dense(a, d->dtype, s)));
+  return from_hip(twell::launch_bwd_sparse(a, d->dtype, s));
 }
 
 twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* w_gate_t, twell_act act,

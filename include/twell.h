@@ -202,8 +202,9 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
  * the same x.  Rows in route->ell_rows use only their stored TwELL slots (a
  * row the forward served lossily from TwELL is differentiated the same way);
  * rows in route->dense_rows are recomputed densely on MFMA.
- * Deterministic: the weight gradients of each neuron are summed in ascending
- * token order (bitwise the same on any device).  dx of the ELL rows comes from
+ * Deterministic: each neuron's weight gradient is the sum of its ELL rows'
+ * terms in ascending token order, plus the dense rows' GEMM result (bitwise
+ * the same on any device).  dx of the ELL rows comes from
  * a lockstep kernel dispatched once per generation of resident workgroups like
  * twell_ffn_fwd's, with the same dependence of its bits on the CU count.
  * ws: twell_sizes(d, route->max_dense_rows).ws_bwd bytes. */
