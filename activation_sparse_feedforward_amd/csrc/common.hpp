@@ -144,6 +144,51 @@ template <> __device__ __forceinline__ void store_bits<EF32>(void* p, int64_t i,
   static_cast<uint32_t*>(p)[i] = bits;
 }
 
+// Which of its workgroup's kWaves * TPW rows each wave of a lockstep kernel takes.  Every chunk ends at
+// a workgroup barrier, so a chunk lasts as long as its busiest wave; rows are
+// therefore dealt by their entry counts: ranked by total count (ties by
+// position), then snaked over the waves (rank r < kWaves to wave r, the next
+// kWaves to waves kWaves - 1 .. 0, and so on), so each wave pairs a busy row with a quiet
+// one.  src[k] = the row-list position of the wave's k-th row.  A row's
+// result does not depend on which wave of the workgroup computes it.  Every
+// thread of the workgroup must call this (one barrier).  tot: kWaves * TPW
+// ints of LDS that the caller does not touch again before its next barrier.
+template <int kWaves, int TPW>
+__device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t* rows, int64_t n_rows, int n_t,
+                                             int64_t blk, int wave, int lane, int* tot, int64_t* src) {
+  constexpr int kNS = kWaves * TPW;
+  static_assert(kNS <= kWave, "one lane per row of the workgroup");
+  const int64_t base = blk * kNS;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int64_t i_row = base + wave * TPW + k;
+    const bool live = i_row < n_rows;  // uniform
+    const int64_t t = live ? (rows ? static_cast<int64_t>(rows[i_row]) : i_row) : 0;
+    float sum = 0.f;  // exact: at most n_t * 128 < 2^24
+    if (live)
+      for (int b = lane; b < n_t; b += kWave) sum += static_cast<float>(max(count[t * n_t + b], 0));
+    sum = wave_sum(sum);
+    if (lane == 0) tot[wave * TPW + k] = live ? static_cast<int>(sum) : -1;
+  }
+  __syncthreads();
+  int rank = 0;
+  if (lane < kNS) {
+    const int tl = tot[lane];
+#pragma unroll 8
+    for (int m = 0; m < kNS; ++m) {
+      const int tm = tot[m];
+      rank += (tm > tl || (tm == tl && m < lane)) ? 1 : 0;
+    }
+  }
+  const int round = rank / kWaves, within = rank % kWaves;
+  const int dw = (round & 1) ? kWaves - 1 - within : within;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kNS && dw == wave && round == k);
+    src[k] = base + (m ? __builtin_ctzll(m) : wave * TPW + k);  // exactly one lane matches
+  }
+}
+
 // ---------------------------------------------------------------- MFMA 32x32 step
 // One "k16 step" of a 32x32 output block: each lane supplies 8 consecutive K
 // elements of its A row (lane % 32) and of its B column (lane % 32), the two

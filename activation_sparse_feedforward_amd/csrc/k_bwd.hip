@@ -477,12 +477,16 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   const int64_t n_rows = p.split_n[0];
   const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
   if (blk * kDxWaves * TPW >= n_rows) return;  // the whole workgroup is past the rows
+  int64_t src[TPW];
+  // the ranking's scratch sits in the entry lists, first written after the
+  // barrier that opens the first chunk
+  balance_rows<kDxWaves, TPW>(p.count, p.light_rows, n_rows, n_t, blk, wave, lane, reinterpret_cast<int*>(smem), src);
   int64_t tk[TPW];
   bool act[TPW];
   float dxf[TPW][NV][kN];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int64_t i_row = (blk * kDxWaves + wave) * TPW + k;
+    const int64_t i_row = src[k];
     act[k] = i_row < n_rows;  // idle rows: the wave still takes part in the barriers
     tk[k] = act[k] ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.light_rows[i_row])) : 0;
 #pragma unroll

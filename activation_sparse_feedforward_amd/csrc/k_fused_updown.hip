@@ -240,7 +240,10 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 // LDS (this frees the VGPRs for the fp32 y accumulators of TPW tokens).  Per
 // token the arithmetic is that of fused_updown_kernel, with the tiles summed
 // starting from the workgroup's rotated chunk (a function of the workgroup
-// index, so results are deterministic for a given row list).
+// index, so results are deterministic for a given row list).  The workgroup's
+// rows are dealt to its waves by their entry counts (balance_rows), which
+// shortens the wait at every chunk barrier and leaves every row's result as it
+// is.
 constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
@@ -261,13 +264,17 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   u32x4_t* xw = xl + wave * TPW * kRowVec;
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
+  int64_t src[TPW];
+  // the ranking's scratch sits in the entry lists, first written after the
+  // barrier that opens the first chunk
+  balance_rows<kSyncWaves, TPW>(p.count, p.rows, n_rows, n_t, blk, wave, lane, reinterpret_cast<int*>(list_all), src);
 
   int64_t tk[TPW];
   bool act[TPW];
   float yf[TPW][NV][kN];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int64_t i_row = (blk * kSyncWaves + wave) * TPW + k;
+    const int64_t i_row = src[k];
     act[k] = i_row < n_rows;  // idle tokens: the wave still takes part in the barriers
     // wave-uniform: keep the token rows in scalar registers
     tk[k] = act[k] ? (p.rows ? static_cast<int64_t>(__builtin_amdgcn_readfirstlane(p.rows[i_row])) : i_row) : 0;
