@@ -144,50 +144,72 @@ template <> __device__ __forceinline__ void store_bits<EF32>(void* p, int64_t i,
   static_cast<uint32_t*>(p)[i] = bits;
 }
 
-// Which of its workgroup's kWaves * TPW rows each wave of a lockstep kernel takes.  Every chunk ends at
-// a workgroup barrier, so a chunk lasts as long as its busiest wave; rows are
-// therefore dealt by their entry counts: ranked by total count (ties by
-// position), then snaked over the waves (rank r < kWaves to wave r, the next
-// kWaves to waves kWaves - 1 .. 0, and so on), so each wave pairs a busy row with a quiet
-// one.  src[k] = the row-list position of the wave's k-th row.  A row's
-// result does not depend on which wave of the workgroup computes it.  Every
-// thread of the workgroup must call this (one barrier).  tot: kWaves * TPW
-// ints of LDS that the caller does not touch again before its next barrier.
-template <int kWaves, int TPW>
+// Which rows each wave of a lockstep kernel takes.  Every chunk ends at a
+// workgroup barrier, so a chunk lasts as long as the workgroup's busiest wave,
+// and the workgroups of an XCD share weight rows through its L2 only while
+// they sweep the tiles at the same pace.  Rows are therefore dealt by their
+// entry counts over windows of win (<= kWin) consecutive workgroups: every workgroup of
+// a window sums the counts of all the window's rows, ranks them (ties by
+// position) and deals them snake-wise over the window's W waves (rank r < W to
+// wave r, the next W to waves W - 1 .. 0, and so on), so each wave pairs a
+// busy row with a quiet one and the window's workgroups carry nearly equal
+// work.  Each workgroup computes the same ranking on its own (no
+// communication between workgroups) and takes its waves' rows.
+//   src[k]: row-list position of the wave's k-th row (>= n_rows: idle)
+//   n_blk:  workgroups of the whole grid (every one of them is launched)
+//   win:    workgroups per window, 1 .. kWin (uniform over the grid)
+//   lds:    2 * kWin * kWaves * TPW ints the caller does not touch before its
+//           next barrier
+// Every thread of the workgroup must call this (two barriers).
+template <int kWaves, int TPW, int kWin>
 __device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t* rows, int64_t n_rows, int n_t,
-                                             int64_t blk, int wave, int lane, int* tot, int64_t* src) {
-  constexpr int kNS = kWaves * TPW;
-  static_assert(kNS <= kWave, "one lane per row of the workgroup");
-  const int64_t base = blk * kNS;
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const int64_t i_row = base + wave * TPW + k;
-    const bool live = i_row < n_rows;  // uniform
-    const int64_t t = live ? (rows ? static_cast<int64_t>(rows[i_row]) : i_row) : 0;
-    float sum = 0.f;  // exact: at most n_t * 128 < 2^24
-    if (live)
-      for (int b = lane; b < n_t; b += kWave) sum += static_cast<float>(max(count[t * n_t + b], 0));
-    sum = wave_sum(sum);
-    if (lane == 0) tot[wave * TPW + k] = live ? static_cast<int>(sum) : -1;
+                                             int64_t blk, int64_t n_blk, int win, int wave, int* lds, int64_t* src) {
+  constexpr int kRpw = kWaves * TPW;  // rows per workgroup
+  constexpr int kThreads = kWaves * kWave;
+  int* tot = lds;
+  int* assign = lds + kWin * kRpw;
+  const int64_t win0 = blk / win * win;
+  const int nwin = static_cast<int>(min(static_cast<int64_t>(win), n_blk - win0));  // workgroups in the window
+  const int nr = nwin * kRpw;
+  const int64_t base = win0 * kRpw;
+  const int tid = threadIdx.x;
+  // row totals: four threads per row, each summing every fourth tile
+  for (int r0 = 0; r0 < nr; r0 += kThreads / 4) {
+    const int r = r0 + tid / 4;
+    const int64_t i_row = base + r;
+    const bool live = r < nr && i_row < n_rows;
+    int s = 0;
+    if (live) {
+      const int64_t t = rows ? static_cast<int64_t>(rows[i_row]) : i_row;
+      for (int b = tid & 3; b < n_t; b += 4) s += max(count[t * n_t + b], 0);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (r < nr && (tid & 3) == 0) tot[r] = live ? s : -1;
   }
   __syncthreads();
-  int rank = 0;
-  if (lane < kNS) {
-    const int tl = tot[lane];
-#pragma unroll 8
-    for (int m = 0; m < kNS; ++m) {
+  const int W = nwin * kWaves;
+  for (int r = tid; r < nr; r += kThreads) {
+    const int tr = tot[r];
+    int rank = 0;
+    for (int m = 0; m < nr; ++m) {
       const int tm = tot[m];
-      rank += (tm > tl || (tm == tl && m < lane)) ? 1 : 0;
+      rank += (tm > tr || (tm == tr && m < r)) ? 1 : 0;
     }
+    const int round = rank / W, within = rank % W;
+    assign[((round & 1) ? W - 1 - within : within) * TPW + round] = r;
   }
-  const int round = rank / kWaves, within = rank % kWaves;
-  const int dw = (round & 1) ? kWaves - 1 - within : within;
+  __syncthreads();
+  const int my = static_cast<int>(blk - win0) * kWaves + wave;
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(lane < kNS && dw == wave && round == k);
-    src[k] = base + (m ? __builtin_ctzll(m) : wave * TPW + k);  // exactly one lane matches
-  }
+  for (int k = 0; k < TPW; ++k) src[k] = base + assign[my * TPW + k];
 }
+
+// Workgroups per row-balancing window of the lockstep kernels on a row list
+// (the hybrid format's light rows, whose densities spread widely); the plain
+// forward (all rows, one density) balances within each workgroup, which costs
+// less at its start.
+constexpr int kBalanceWindow = 8;
 
 // ---------------------------------------------------------------- MFMA 32x32 step
 // One "k16 step" of a 32x32 output block: each lane supplies 8 consecutive K

@@ -476,11 +476,15 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   const int n_t = p.F / tile_n;
   const int64_t n_rows = p.split_n[0];
   const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
-  if (blk * kDxWaves * TPW >= n_rows) return;  // the whole workgroup is past the rows
+  // rows are dealt over windows of workgroups (balance_rows): only a workgroup
+  // whose whole window is past the rows has none
+  if (blk / kBalanceWindow * kBalanceWindow * kDxWaves * TPW >= n_rows) return;
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kDxWaves, TPW>(p.count, p.light_rows, n_rows, n_t, blk, wave, lane, reinterpret_cast<int*>(smem), src);
+  balance_rows<kDxWaves, TPW, kBalanceWindow>(p.count, p.light_rows, n_rows, n_t, blk,
+                                              (p.T + kDxWaves * TPW - 1) / (kDxWaves * TPW), kBalanceWindow, wave,
+                                              reinterpret_cast<int*>(smem), src);
   int64_t tk[TPW];
   bool act[TPW];
   float dxf[TPW][NV][kN];

@@ -240,10 +240,10 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 // LDS (this frees the VGPRs for the fp32 y accumulators of TPW tokens).  Per
 // token the arithmetic is that of fused_updown_kernel, with the tiles summed
 // starting from the workgroup's rotated chunk (a function of the workgroup
-// index, so results are deterministic for a given row list).  The workgroup's
-// rows are dealt to its waves by their entry counts (balance_rows), which
-// shortens the wait at every chunk barrier and leaves every row's result as it
-// is.
+// index, so results are deterministic for a given row list).  Rows are dealt
+// to the waves by their entry counts (balance_rows: within each workgroup for
+// all rows, over windows of 8 workgroups for a row list), which shortens the
+// wait at every chunk barrier and keeps the workgroups in step.
 constexpr int kSyncWaves = 16;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
@@ -259,7 +259,10 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
   const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
-  if (blk * kSyncWaves * TPW >= n_rows) return;  // the whole workgroup is past the rows
+  // rows are dealt over windows of workgroups (balance_rows): only a workgroup
+  // whose whole window is past the rows has none
+  const int win = p.rows ? kBalanceWindow : 1;
+  if (blk / win * win * kSyncWaves * TPW >= n_rows) return;
   int4* list = list_all + wave * kSyncList;
   u32x4_t* xw = xl + wave * TPW * kRowVec;
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
@@ -267,7 +270,9 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kSyncWaves, TPW>(p.count, p.rows, n_rows, n_t, blk, wave, lane, reinterpret_cast<int*>(list_all), src);
+  balance_rows<kSyncWaves, TPW, kBalanceWindow>(p.count, p.rows, n_rows, n_t, blk,
+                                                (p.T + kSyncWaves * TPW - 1) / (kSyncWaves * TPW), win, wave,
+                                                reinterpret_cast<int*>(list_all), src);
 
   int64_t tk[TPW];
   bool act[TPW];
