@@ -158,12 +158,14 @@ template <> __device__ __forceinline__ void store_bits<EF32>(void* p, int64_t i,
 //   src[k]: row-list position of the wave's k-th row (>= n_rows: idle)
 //   n_blk:  workgroups of the whole grid (every one of them is launched)
 //   win:    workgroups per window, 1 .. kWin (uniform over the grid)
-//   lds:    2 * kWin * kWaves * TPW ints the caller does not touch before its
-//           next barrier
+//   lds:    2 * kWin * kWaves * TPW ints, 16-byte aligned, that the caller
+//           does not touch before its next barrier
+//   row_total: per-token sum of the counts, or null (then summed here)
 // Every thread of the workgroup must call this (two barriers).
 template <int kWaves, int TPW, int kWin>
-__device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t* rows, int64_t n_rows, int n_t,
-                                             int64_t blk, int64_t n_blk, int win, int wave, int* lds, int64_t* src) {
+__device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t* row_total, const int32_t* rows,
+                                             int64_t n_rows, int n_t, int64_t blk, int64_t n_blk, int win, int wave,
+                                             int* lds, int64_t* src) {
   constexpr int kRpw = kWaves * TPW;  // rows per workgroup
   constexpr int kThreads = kWaves * kWave;
   int* tot = lds;
@@ -173,7 +175,14 @@ __device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t
   const int nr = nwin * kRpw;
   const int64_t base = win0 * kRpw;
   const int tid = threadIdx.x;
-  // row totals: four threads per row, each summing every fourth tile
+  // row totals: read from row_total[token] where the caller has them, else
+  // four threads per row, each summing every fourth tile
+  if (row_total) {
+    for (int r = tid; r < nr; r += kThreads) {
+      const int64_t i_row = base + r;
+      tot[r] = i_row < n_rows ? row_total[rows ? static_cast<int64_t>(rows[i_row]) : i_row] : -1;
+    }
+  } else
   for (int r0 = 0; r0 < nr; r0 += kThreads / 4) {
     const int r = r0 + tid / 4;
     const int64_t i_row = base + r;
@@ -192,9 +201,15 @@ __device__ __forceinline__ void balance_rows(const int32_t* count, const int32_t
   for (int r = tid; r < nr; r += kThreads) {
     const int tr = tot[r];
     int rank = 0;
-    for (int m = 0; m < nr; ++m) {
-      const int tm = tot[m];
-      rank += (tm > tr || (tm == tr && m < r)) ? 1 : 0;
+    // four totals per LDS read (nr is a multiple of 4, tot 16-byte aligned),
+    // several reads in flight: the LDS latency is not paid once per row
+#pragma unroll 4
+    for (int m = 0; m < nr; m += 4) {
+      const int4 tm = *reinterpret_cast<const int4*>(tot + m);
+      rank += (tm.x > tr || (tm.x == tr && m < r)) ? 1 : 0;
+      rank += (tm.y > tr || (tm.y == tr && m + 1 < r)) ? 1 : 0;
+      rank += (tm.z > tr || (tm.z == tr && m + 2 < r)) ? 1 : 0;
+      rank += (tm.w > tr || (tm.w == tr && m + 3 < r)) ? 1 : 0;
     }
     const int round = rank / W, within = rank % W;
     assign[((round & 1) ? W - 1 - within : within) * TPW + round] = r;

@@ -29,6 +29,7 @@ struct FusedArgs {
   void* y;             // [T x d]
   const int32_t* rows;        // row list (ELL rows of the hybrid format) or null = all rows
   const int32_t* n_rows_dev;  // device count of `rows` or null
+  const int32_t* row_total;   // [T] sum of each token's counts, or null (lockstep row balancing)
   int64_t T;                  // rows of x / y; also the upper bound of the row list
   int32_t d, F, tile_n, C;
   // split mode (launch_fused_split): every row of the list is cut into

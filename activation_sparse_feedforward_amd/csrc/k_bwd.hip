@@ -482,7 +482,7 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kDxWaves, TPW, kBalanceWindow>(p.count, p.light_rows, n_rows, n_t, blk,
+  balance_rows<kDxWaves, TPW, kBalanceWindow>(p.count, p.row_total, p.light_rows, n_rows, n_t, blk,
                                               (p.T + kDxWaves * TPW - 1) / (kDxWaves * TPW), kBalanceWindow, wave,
                                               reinterpret_cast<int*>(smem), src);
   int64_t tk[TPW];

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kSyncWaves, TPW, kBalanceWindow>(p.count, p.rows, n_rows, n_t, blk,
+  balance_rows<kSyncWaves, TPW, kBalanceWindow>(p.count, p.row_total, p.rows, n_rows, n_t, blk,
                                                 (p.T + kSyncWaves * TPW - 1) / (kSyncWaves * TPW), win, wave,
                                                 reinterpret_cast<int*>(list_all), src);
 

@@ -221,6 +221,7 @@ twell_status hybrid_launch(const twell_desc* d, const void* x, const void* w_gat
   f.y = y;
   f.rows = r.light_rows;
   f.n_rows_dev = r.split_n + 0;
+  f.row_total = r.row_total;  // written by the route pass above
   f.T = d->T;
   f.d = d->d_model;
   f.F = d->d_ff;
