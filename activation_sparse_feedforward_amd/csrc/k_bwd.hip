@@ -40,6 +40,7 @@
 // Per pair each pass gathers two rows (x[t] and dy[t], then W_gate^T[j] and
 // W_up^T[j]), and both dot products sit in the per-neuron pass, where one of
 // their operands is already in registers.
+#include "balance.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 

@@ -16,6 +16,7 @@
 //   y[t] += (a_j * u_j) * W_down[j]   (coalesced 16-byte loads, fp32 FMAs)
 // and finally writes y[t] once.  The walk is bound by the gather of the two
 // weight rows per active neuron, which are served mostly from the MALL.
+#include "balance.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 

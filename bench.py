@@ -74,7 +74,7 @@ def parse():
 # sources whose change invalidates a kernel's measured counters
 KERNEL_SOURCES = {
     "gate_pack": ["k_gate_pack.hip", "gemm256.hpp", "gemm_core.hpp", "common.hpp"],
-    "fused_updown": ["k_fused_updown.hip", "common.hpp"],
+    "fused_updown": ["k_fused_updown.hip", "balance.hpp", "common.hpp"],
 }
 # substrings of the dispatch names of each kernel
 KERNEL_NAMES = {"gate_pack": "gate_pack", "fused_updown": "fused_updown", "calib_copy": "neg_kernel"}
