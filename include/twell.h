@@ -155,7 +155,8 @@ twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* 
  * ceil(ceil(T / (16 R)) / CUs) dispatches of the same kernel, e.g. 2 at
  * T = 16384, d_model = 2048 (R = 2) and 1 at T = 8192, d_model = 1024 (R = 2)
  * on a 256-CU MI355X.  Every row is computed start to finish by one workgroup
- * of one dispatch.
+ * of one dispatch; a workgroup deals its rows to its waves by their entry
+ * counts (a row's result does not depend on the wave).
  * Bits: each row's tiles are summed starting at a chunk that depends on its
  * workgroup's index and generation, hence on the device's CU count; y is
  * bitwise reproducible on one device (and on devices with the same CU count),
@@ -181,8 +182,10 @@ twell_status twell_ffn_fwd(const twell_desc* d, const void* x, twell_act act, co
  *   3.   fused up/down (as twell_ffn_fwd) over ell_rows; ELL rows with far
  *        more non-zeros than the batch's mean row (> max(2 slots, 2 x mean),
  *        at most 1024 of them) are cut into tile ranges processed in parallel
- *        and summed in a fixed order, so their y can differ from
- *        twell_ffn_fwd's in the last bits (deterministic either way);
+ *        and summed in a fixed order; the other ELL rows are dealt over
+ *        windows of 8 lockstep workgroups by their entry counts.  Which
+ *        workgroup computes a row therefore differs from twell_ffn_fwd, so its
+ *        y can differ in the last bits (deterministic either way);
  *   4-5. dense gate|up GEMM over the gathered dense rows (h = ReLU(g) * u,
  *        recomputed, kept in ws), then the down GEMM scattered into y.
  * y [T x d_model] is overwritten.  ws: twell_sizes(d, max_dense_rows).ws_hybrid bytes. */
