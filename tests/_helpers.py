@@ -90,6 +90,17 @@ def check_guards(*tensors):
         assert bool(torch.all(tail == CANARY)), f"write past the end of a buffer of {n} bytes"
 
 
+def assert_rows_written(t: torch.Tensor, label: str):
+    """Every row of an output made by ``guarded`` was written: no row still
+    holds the 0xA5 fill in every byte (a dropped row shows up here even where
+    the float64 checks only sample rows)."""
+    if t.numel() == 0:
+        return
+    b = t.contiguous().view(torch.uint8).reshape(t.shape[0], -1)
+    left = torch.nonzero((b == 0xA5).all(dim=1)).flatten()
+    assert left.numel() == 0, f"{label}: {left.numel()} rows never written (first: {left[:8].tolist()})"
+
+
 def guarded_act(desc):
     """TwELL planes in guarded buffers."""
     return T.Act(guarded((desc.T, desc.n_t), torch.int32),

@@ -15,7 +15,7 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import check_guards, desc_for, dev, guarded, host64, poison_, say, within
+from _helpers import assert_rows_written, check_guards, desc_for, dev, guarded, host64, poison_, say, within
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-5, "bf16": 1e-2}
@@ -39,6 +39,9 @@ def run_bwd(w, cap, l1=2e-5, label="", check=True):
     T.twell_ffn_bwd(desc, x, act, route, wg, wu, wd, dy, l1, dx, *dws, wsb)
     torch.cuda.synchronize()
     check_guards(wsb, dx, *dws)
+    assert_rows_written(dx, "dx")
+    for name, t in zip(("dw_gate_t", "dw_up_t", "dw_down"), dws):
+        assert_rows_written(t, name)
     out = dict(dx=dx, dws=dws, act=act, route=route, desc=desc, tensors=(x, wg, wu, wd, dy), wsb=wsb, gate=gate)
     if not check:
         return out

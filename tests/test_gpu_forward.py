@@ -23,7 +23,8 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import check_guards, desc_for, dev, guarded, guarded_act, host64, record, say, within
+from _helpers import (assert_rows_written, check_guards, desc_for, dev, guarded, guarded_act, host64, record, say,
+                      within)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +45,7 @@ def _run_pack_fwd(w, desc, inp, dbg=True):
     T.twell_ffn_fwd(desc, x, act, wu, wd, y)
     torch.cuda.synchronize()
     check_guards(*act, stats, y, *([gate] if dbg else []))
+    assert_rows_written(y, "y")
     return dict(x=x, wg=wg, wu=wu, wd=wd, act=act, stats=stats, gate=gate, y=y)
 
 

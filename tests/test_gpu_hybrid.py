@@ -15,7 +15,8 @@ import torch
 from activation_sparse_feedforward_amd import twell as T
 from activation_sparse_feedforward_amd import workloads as W
 from oracle import twell_oracle as O
-from _helpers import check_guards, desc_for, dev, guarded, guarded_act, guarded_route, host64, poison_, say, within
+from _helpers import (assert_rows_written, check_guards, desc_for, dev, guarded, guarded_act, guarded_route, host64,
+                      poison_, say, within)
 
 pytestmark = pytest.mark.gpu
 TOL = {"fp32": 1e-5, "bf16": 1e-2}
@@ -34,6 +35,7 @@ def run_hybrid(w, cap, rows=None, label=""):
     T.twell_ffn_fwd_hybrid(desc, x, wg, act, wu, wd, y, route, ws)
     torch.cuda.synchronize()
     check_guards(*act, *route, ws, y)
+    assert_rows_written(y, "hybrid y")
 
     count = act.count.cpu().numpy()
     idx = act.idx.cpu().numpy()
