@@ -124,6 +124,15 @@ def test_hybrid_full_size_sampled():
     run_hybrid(w, 1024, rows=rows, label="full c4")
 
 
+def test_hybrid_lockstep_four_rows_per_wave_sampled():
+    # d_model = 1024 at 16384 rows: the lockstep kernel holds 4 rows per wave, so
+    # its row dealing ranks 512 rows per window of 8 workgroups
+    w = W.workload(4, d_model=1024, d_ff=4096)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(w.T - 128, w.T), rng.choice(w.T, 256, replace=False)]))
+    run_hybrid(w, 1024, rows=rows, label="lognormal d=1024")
+
+
 def test_hybrid_deterministic_lockstep():
     """A batch large enough for the lockstep fused kernel (whose chunk order
     depends on the workgroup), with heavy and dense rows: two calls give the
