@@ -536,112 +536,177 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
 }
 
 // Small batches (T <= 64, bf16, T_n = 128): the work is reading W_gate once, so
-// the tiling is turned around.  One workgroup per TwELL tile (128 neurons),
-// 4 waves of 32 neurons each; the neurons are the MFMA's M side and the tokens
-// its N side (one 32-token block, two above 32 tokens).  With only F/128
-// workgroups, each must keep a lot of its weight stream in flight: 128-byte K
-// slices of the 128 weight rows (16 KB) and of XR token rows (XR = 16, 32 or
-// 64: the batch rounded up) move global -> LDS with direct loads through a
-// ring of NS stages, as many as the LDS holds (8, 7 and 6), and the wait
-// before using a slice lets the younger stages stay in flight.  ReLU(g),
-// rounded to bf16, is then staged in LDS as [token][128] and each wave packs a
-// quarter of the tokens: lane l holds columns 2l, 2l + 1, and ballots give the
-// slots in ascending column order.  Same stored values and format as the
-// large-batch kernels.
+// the tiling is turned around.  One workgroup per TwELL tile (128 neurons); the
+// neurons are the MFMA's M side and the tokens its N side.  With only F/128
+// workgroups each CU must stream its tile's 128 weight rows fast, and what
+// limits it is the trip through LDS, not HBM: coalesced 16-byte register loads
+// (8 rows x 128 bytes per wave instruction; loads in MFMA-fragment order touch
+// two to four times as many cache lines per instruction and stream far slower)
+// fetch each 128-byte K slice of the 128 weight rows and of XR token rows (XR =
+// 16, 32 or 64: the batch rounded up) kSmallAhead slices ahead, and a slice is
+// stored into a two-slice LDS ring just before its one barrier.  Eight waves
+// form two groups of four; in a group, wave w takes neurons 32w .. 32w + 31,
+// and the two groups take alternate k-steps of every slice, so each MFMA chain
+// is half as long; group 1 parks its partial sums in LDS after the loop and
+// group 0 adds them (a fixed order).  Up to 16 tokens the MFMA is 16x16x32
+// (16 neurons x 16 tokens), above that 32x32x16 (one 32-token block, two
+// above 32 tokens).  ReLU(g), rounded to bf16, is then staged in LDS as
+// [token][128] and each wave packs every 8th token: lane l holds columns 2l,
+// 2l + 1, and ballots give the slots in ascending column order.  Same stored
+// values and format as the large-batch kernels.
 constexpr int kSmallT = 64;
+constexpr int kSmallWaves = 8;   // two groups of 4 waves
+constexpr int kSmallAhead = 4;   // K slices in flight in registers (d / 64 is a multiple of 8)
 
-template <int XR, int NS>
-__global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
-  constexpr int kStage = (128 + XR) * 128;  // W slice + XR token rows
-  // direct loads of one stage per wave: rows 8 (4q + wave) + lane / 8 for q = 0, 1, ...
-  // up to 128 + XR rows; with XR = 16 waves 2 and 3 issue one fewer
-  constexpr int kLoadsFull = (128 + XR + 31) / 32, kLoadsShort = (128 + XR) / 32;
+template <int XR>
+__global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(PackArgs p) {
+  constexpr bool kM16 = XR == 16;
+  constexpr int kSlice = (128 + XR) * 128;  // one LDS slice: 128 weight rows, then XR token rows
+  // load round q of wave w covers slice rows 8 (8q + w) + lane / 8; the last
+  // round reaches past the slice for the higher waves ("short" waves): their
+  // load there re-reads the clamped last row and is not stored, so every wave
+  // issues the same number of loads and the compiler's wait counts stay exact
+  constexpr int kRounds = (128 + XR + 8 * kSmallWaves - 1) / (8 * kSmallWaves);
+  constexpr int kRoundsShort = (128 + XR) / (8 * kSmallWaves);
   extern __shared__ __align__(16) char lds[];
   __shared__ uint32_t ovf_s, nnz_s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31;
-  const int b = blockIdx.x;  // TwELL tile
+  const int ng = wave & 3, kg = wave >> 2;  // neuron group (32 neurons), k-step group
+  const int b = blockIdx.x;                 // TwELL tile
   const int n_t = p.F / 128;
   const int T = static_cast<int>(p.T);
   if (threadIdx.x == 0) {
     ovf_s = 0;
     nnz_s = 0;
   }
-  // direct-load sources: instruction q of wave w fills stage rows 8*(4q + w) + lane/8,
-  // rows 0..127 = weight rows, 128..127 + XR = token rows (clamped to T - 1)
-  // (a fixed-size array: with its size a template constant, captured by the
-  // lambda below, the host pass of hipcc emitted no launch stub for the kernel)
-  const char* src[6];
-  static_assert(kLoadsFull <= 6, "load rounds");
+  const char* src[kRounds];
+  int dst[kRounds];
 #pragma unroll
-  for (int q = 0; q < kLoadsFull; ++q) {
-    const int r = min(8 * (4 * q + wave) + (lane >> 3), 127 + XR);  // (the clamp only feeds unissued loads)
-    const int c = (lane & 7) ^ lds_swz(r);
+  for (int q = 0; q < kRounds; ++q) {
+    const int r = min(8 * (kSmallWaves * q + wave) + (lane >> 3), 127 + XR);
     const char* base = r < 128 ? static_cast<const char*>(p.w_gate_t) +
                                      (static_cast<int64_t>(b) * 128 + r) * p.d * 2
                                : static_cast<const char*>(p.x) + static_cast<int64_t>(min(r - 128, T - 1)) * p.d * 2;
-    src[q] = base + c * 16;
+    src[q] = base + ((lane & 7) ^ lds_swz(r)) * 16;  // chunk c of the row lands in swizzled place
+    dst[q] = r * 128 + (lane & 7) * 16;
   }
-  const bool short_wave = 8 * (4 * kLoadsShort + wave) >= 128 + XR;  // wave-uniform
-  auto issue = [&](int kt) {
-    char* st = lds + (kt % NS) * kStage;
+  const bool short_wave = 8 * (kSmallWaves * kRoundsShort + wave) >= 128 + XR;  // wave-uniform
+  u32x4_t rg[kSmallAhead][kRounds];
+  const int nk = p.d / 64;  // 128-byte slices
 #pragma unroll
-    for (int q = 0; q < kLoadsFull; ++q)
-      if (q < kLoadsShort || !short_wave)
-        __builtin_amdgcn_global_load_lds(src[q] + static_cast<int64_t>(kt) * 128, st + (4 * q + wave) * 8 * 128, 16,
-                                         0, 0);
-  };
-  const int nk = p.d / 64;  // 128-byte slices; d is a multiple of 512, so nk >= 8 >= NS - 1
+  for (int j = 0; j < kSmallAhead; ++j)
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) rg[j][q] = *reinterpret_cast<const u32x4_t*>(src[q] + j * 128);
   const bool two = XR > 32 && T > 32;
-  f32x16_t acc0, acc1;
+  f32x16_t acc0, acc1;  // 32x32x16: this wave's 32 neurons x 32 tokens (acc1: tokens 32..63)
+  f32x4_t a16[2];       // 16x16x32: neurons 32 ng + 16 h .. + 15 x 16 tokens
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
 #pragma unroll
-  for (int q = 0; q < NS - 1; ++q)
-    if (q < nk) issue(q);
-  for (int kt = 0; kt < nk; ++kt) {
-    // slice kt landed when at most the (NS - 2) younger slices' loads are outstanding
-    if (kt + NS - 1 <= nk) {
-      if (short_wave)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NS - 2) * kLoadsShort) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NS - 2) * kLoadsFull) : "memory");
+  for (int i = 0; i < 4; ++i) a16[0][i] = a16[1][i] = 0.f;
+  auto slice = [&](int kt, u32x4_t(&v)[kRounds], bool more) {
+    // ring slot kt & 1 was last read in iteration kt - 2, which every wave
+    // finished before the barrier of iteration kt - 1
+    char* st = lds + (kt & 1) * kSlice;
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q)
+      if (q < kRoundsShort || !short_wave) *reinterpret_cast<u32x4_t*>(st + dst[q]) = v[q];
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < kRounds; ++q)
+        v[q] = *reinterpret_cast<const u32x4_t*>(src[q] + static_cast<int64_t>(kt + kSmallAhead) * 128);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (kM16) {
+      // k32 step kg of the slice: lane l supplies 8 k-values (chunk 4 kg + l / 16) of
+      // its neuron (A) and its token (B) row l % 16
+      const int c = 4 * kg + (lane >> 4);
+      const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(st + lds_off(128 + (lane & 15), c));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t fa = *reinterpret_cast<const u32x4_t*>(st + lds_off(32 * ng + 16 * h + (lane & 15), c));
+        a16[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa),
+                                                        __builtin_bit_cast(bf16x8_t, fb), a16[h], 0, 0, 0);
+      }
     } else {
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    }
-    // the stage refilled now was last read in iteration kt - 1, which every
-    // wave finished before the barrier above
-    if (kt + NS - 1 < nk) issue(kt + NS - 1);
-    const char* st = lds + (kt % NS) * kStage;
-    Frag<EBf16> fa[4], fb0[4], fb1[4];
+      // k16 steps kg and kg + 2 of the slice; tokens past XR (past T) read the
+      // last loaded token row, their outputs are discarded
+      Frag<EBf16> fa[2], fb0[2], fb1[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      read_frag256(fa[kk], st, wave * 32 + li, kk, lane);
-      // tokens past XR (past T) read the last loaded token row: their outputs are discarded
-      read_frag256(fb0[kk], st, 128 + min(li, XR - 1), kk, lane);
-      if constexpr (XR > 32) read_frag256(fb1[kk], st, 160 + li, kk, lane);
-    }
+      for (int j = 0; j < 2; ++j) {
+        read_frag256(fa[j], st, 32 * ng + li, kg + 2 * j, lane);
+        read_frag256(fb0[j], st, 128 + min(li, XR - 1), kg + 2 * j, lane);
+        if constexpr (XR > 32) read_frag256(fb1[j], st, 160 + li, kg + 2 * j, lane);
+      }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      mfma_k16(acc0, fa[kk], fb0[kk]);
-      if (two) mfma_k16(acc1, fa[kk], fb1[kk]);
+      for (int j = 0; j < 2; ++j) {
+        mfma_k16(acc0, fa[j], fb0[j]);
+        if (two) mfma_k16(acc1, fa[j], fb1[j]);
+      }
     }
+  };
+  // the last kSmallAhead slices issue no loads (peeled, so the loop's loads are unconditional)
+  for (int kt0 = 0; kt0 < nk - kSmallAhead; kt0 += kSmallAhead) {
+#pragma unroll
+    for (int j = 0; j < kSmallAhead; ++j) slice(kt0 + j, rg[j], true);
   }
-  __syncthreads();  // all loads done, every wave past its last reads: reuse the ring
-  uint16_t(*gl)[128] = reinterpret_cast<uint16_t(*)[128]>(lds);  // [64][128]
-  // acc register r of lane l: neuron 32*wave + acc_row(r, l), token (block) l % 32
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int col = wave * 32 + acc_row(r, lane);
-    const float g0 = acc0[r], g1 = acc1[r];
-    if (li < T) gl[li][col] = static_cast<uint16_t>(round_store<EBf16>(g0 > 0.f ? g0 : 0.f).bits);
-    if (two && 32 + li < T) gl[32 + li][col] = static_cast<uint16_t>(round_store<EBf16>(g1 > 0.f ? g1 : 0.f).bits);
+  for (int j = 0; j < kSmallAhead; ++j) slice(nk - kSmallAhead + j, rg[j], false);
+  __syncthreads();  // every wave past its last ring reads: reuse the LDS
+  // group 1's partials at [wave ng][register][lane] (16 KB per token block),
+  // then the staged rows [64][128] bf16 at 32 KB
+  float* red = reinterpret_cast<float*>(lds);
+  uint16_t(*gl)[128] = reinterpret_cast<uint16_t(*)[128]>(lds + 32 * 1024);
+  if (kg == 1) {
+    float* o = red + ng * 1024 + lane;
+    if constexpr (kM16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[(4 * h + i) * 64] = a16[h][i];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[r * 64] = acc0[r];
+        if (two) o[4096 + r * 64] = acc1[r];
+      }
+    }
   }
   __syncthreads();
-  // pack: wave w takes tokens w, w + 4, ...; lane l holds columns 2l and 2l + 1
+  if (kg == 0) {
+    const float* o = red + ng * 1024 + lane;
+    if constexpr (kM16) {
+      // 16x16 accumulator: register i of lane l holds row 4 (l / 16) + i, column l % 16
+      const int tok = lane & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float g = a16[h][i] + o[(4 * h + i) * 64];
+          if (tok < T)
+            gl[tok][32 * ng + 16 * h + 4 * (lane >> 4) + i] =
+                static_cast<uint16_t>(round_store<EBf16>(g > 0.f ? g : 0.f).bits);
+        }
+    } else {
+      // acc register r of lane l: neuron 32 ng + acc_row(r, l), token (block) l % 32
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = 32 * ng + acc_row(r, lane);
+        const float g0 = acc0[r] + o[r * 64];
+        if (li < T) gl[li][col] = static_cast<uint16_t>(round_store<EBf16>(g0 > 0.f ? g0 : 0.f).bits);
+        if (two) {
+          const float g1 = acc1[r] + o[4096 + r * 64];
+          if (32 + li < T) gl[32 + li][col] = static_cast<uint16_t>(round_store<EBf16>(g1 > 0.f ? g1 : 0.f).bits);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // pack: wave w takes tokens w, w + 8, ...; lane l holds columns 2l and 2l + 1
   const int C = p.C;
   uint32_t ovf = 0, nnz = 0;
-  for (int t = wave; t < T; t += 4) {
+  for (int t = wave; t < T; t += kSmallWaves) {
     const uint32_t v0 = gl[t][2 * lane], v1 = gl[t][2 * lane + 1];
     if (p.gate_dbg) {
       uint16_t* gd = static_cast<uint16_t*>(p.gate_dbg) + static_cast<int64_t>(t) * p.F + b * 128 + 2 * lane;
@@ -688,23 +753,24 @@ __global__ __launch_bounds__(256, 1) void gate_pack_small_kernel(PackArgs p) {
   }
 }
 
-template <int XR, int NS>
+template <int XR>
 static hipError_t launch_pack_small_t(const PackArgs& a, hipStream_t s) {
-  constexpr int lds = NS * (128 + XR) * 128;
-  static_assert(lds >= 64 * 128 * 2, "the pack stages [64][128] bf16 in the ring");
+  constexpr int kRing = 2 * (128 + XR) * 128;
+  constexpr int kEpilogue = 32 * 1024 + 64 * 128 * 2;  // partial sums, then staged rows
+  constexpr int lds = kRing > kEpilogue ? kRing : kEpilogue;
   static_assert(lds + 64 <= 160 * 1024, "LDS of one workgroup");
-  static_assert(NS - 1 <= 8 && (NS - 2) * ((128 + XR + 31) / 32) <= 63, "prologue depth / vmcnt range");
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel<XR, NS>),
+  static_assert(kSmallWaves == 8 && 8 % kSmallAhead == 0, "two wave groups; slices a multiple of the prefetch");
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel<XR>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gate_pack_small_kernel<XR, NS>), dim3(a.F / 128), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((gate_pack_small_kernel<XR>), dim3(a.F / 128), dim3(kSmallWaves * 64), lds, s, a);
   return hipGetLastError();
 }
 
 static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
-  if (a.T <= 16) return launch_pack_small_t<16, 8>(a, s);
-  if (a.T <= 32) return launch_pack_small_t<32, 7>(a, s);
-  return launch_pack_small_t<64, 6>(a, s);
+  if (a.T <= 16) return launch_pack_small_t<16>(a, s);
+  if (a.T <= 32) return launch_pack_small_t<32>(a, s);
+  return launch_pack_small_t<64>(a, s);
 }
 
 template <class E>

@@ -10,6 +10,7 @@ still works, but every call raises: there is no CPU fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 from typing import NamedTuple, Optional
@@ -134,12 +135,25 @@ class Route(NamedTuple):
         return int(self.dense_rows.numel())
 
 
-def sizes(desc: Desc, max_dense_rows: int = 0) -> dict:
+# The entry points below share one C struct and one size table per descriptor
+# (the library only reads the struct): at small batches the host cost of a
+# call, not the kernels, sets the pace of a step.
+@functools.lru_cache(maxsize=256)
+def _cdesc(desc: Desc) -> CDesc:
+    return desc.c()
+
+
+@functools.lru_cache(maxsize=256)
+def _sizes(desc: Desc, max_dense_rows: int) -> dict:
     out = CSizes()
-    st = library().twell_sizes(ctypes.byref(desc.c()), ctypes.c_int64(max_dense_rows), ctypes.byref(out))
+    st = library().twell_sizes(ctypes.byref(_cdesc(desc)), ctypes.c_int64(max_dense_rows), ctypes.byref(out))
     if st != TWELL_OK:
         raise TwellError("twell_sizes", st)
     return {k: int(getattr(out, k)) for k, _ in CSizes._fields_}
+
+
+def sizes(desc: Desc, max_dense_rows: int = 0) -> dict:
+    return dict(_sizes(desc, int(max_dense_rows)))
 
 
 def alloc_act(desc: Desc, device="cuda") -> Act:
@@ -161,14 +175,14 @@ def _ptr(t: Optional[torch.Tensor], name: str, nbytes: int, dtype: Optional[torc
         return 0
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name}: must be a GPU tensor (got {t.device})")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
-    if t.numel() * t.element_size() < nbytes:
-        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, need {nbytes}")
+    if t.nbytes < nbytes:
+        raise ValueError(f"{name}: {t.nbytes} bytes, need {nbytes}")
     return t.data_ptr()
 
 
@@ -179,7 +193,7 @@ def _stream(stream) -> int:
 
 
 def _act(desc: Desc, act: Act) -> CAct:
-    sz = sizes(desc)
+    sz = _sizes(desc, 0)
     return CAct(_ptr(act.count, "count", sz["count"], torch.int32),
                 _ptr(act.idx, "idx", sz["idx"], torch.uint8),
                 _ptr(act.val, "val", sz["val"], desc.torch_dtype))
@@ -204,7 +218,7 @@ def twell_pack(desc: Desc, x, w_gate_t, act: Act, stats=None, gate_dbg=None, str
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
     _check("twell_pack", library().twell_pack(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt),
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
         _ptr(stats, "stats", 16, torch.int64), _ptr(gate_dbg, "gate_dbg", desc.T * desc.d_ff * e, dt),
         _stream(stream)))
@@ -215,9 +229,9 @@ def twell_pack_classic(desc: Desc, x, w_gate_t, act: Act, ws, stream=None):
     to the same TwELL planes (see include/twell.h)."""
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
-    need = sizes(desc)["ws_pack_classic"]
+    need = _sizes(desc, 0)["ws_pack_classic"]
     _check("twell_pack_classic", library().twell_pack_classic(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt),
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act), _ptr(ws, "ws", need),
         ctypes.c_size_t(ws.numel() * ws.element_size() if ws is not None else 0), _stream(stream)))
 
@@ -228,7 +242,7 @@ def twell_ffn_fwd(desc: Desc, x, act: Act, w_up_t, w_down, y, stream=None):
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
     _check("twell_ffn_fwd", library().twell_ffn_fwd(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt), _act(desc, act),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt), _act(desc, act),
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
         _ptr(y, "y", desc.T * desc.d_model * e, dt), _stream(stream)))
@@ -238,10 +252,10 @@ def twell_ffn_fwd_hybrid(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_down, y, r
     """Router + fused TwELL path on ELL rows + dense MFMA fallback on dense rows."""
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
-    need = sizes(desc, route.max_dense_rows)["ws_hybrid"]
+    need = _sizes(desc, route.max_dense_rows)["ws_hybrid"]
     cr = _route(desc, route)
     _check("twell_ffn_fwd_hybrid", library().twell_ffn_fwd_hybrid(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt),
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
@@ -258,7 +272,7 @@ def twell_ffn_fwd_hybrid_noalloc(desc: Desc, x, w_gate_t, act: Act, w_up_t, w_do
     dt = desc.torch_dtype
     cr = _route(desc, route)
     _check("twell_ffn_fwd_hybrid_noalloc", library().twell_ffn_fwd_hybrid_noalloc(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt),
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt), _act(desc, act),
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
@@ -270,11 +284,11 @@ def twell_ffn_bwd(desc: Desc, x, act: Act, route: Route, w_gate_t, w_up_t, w_dow
     """Backward of the hybrid-format FFN with the L1 activation penalty (see include/twell.h)."""
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
-    need = sizes(desc, route.max_dense_rows)["ws_bwd"]
+    need = _sizes(desc, route.max_dense_rows)["ws_bwd"]
     cr = _route(desc, route)
     wbytes = desc.d_ff * desc.d_model
     _check("twell_ffn_bwd", library().twell_ffn_bwd(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt), _act(desc, act), ctypes.byref(cr),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt), _act(desc, act), ctypes.byref(cr),
         _ptr(w_gate_t, "w_gate_t", wbytes * e, dt), _ptr(w_up_t, "w_up_t", wbytes * e, dt),
         _ptr(w_down, "w_down", wbytes * e, dt), _ptr(dy, "dy", desc.T * desc.d_model * e, dt),
         ctypes.c_float(l1_coef), _ptr(dx, "dx", desc.T * desc.d_model * e, dt),
@@ -287,9 +301,9 @@ def twell_dense_ffn_fwd(desc: Desc, x, w_gate_t, w_up_t, w_down, y, ws, stream=N
     """The library's dense MFMA FFN (gate|up GEMM with ReLU*u epilogue, then down)."""
     e = 2 if desc.dtype == "bf16" else 4
     dt = desc.torch_dtype
-    need = sizes(desc)["ws_dense_fwd"]
+    need = _sizes(desc, 0)["ws_dense_fwd"]
     _check("twell_dense_ffn_fwd", library().twell_dense_ffn_fwd(
-        ctypes.byref(desc.c()), _ptr(x, "x", desc.T * desc.d_model * e, dt),
+        ctypes.byref(_cdesc(desc)), _ptr(x, "x", desc.T * desc.d_model * e, dt),
         _ptr(w_gate_t, "w_gate_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_up_t, "w_up_t", desc.d_ff * desc.d_model * e, dt),
         _ptr(w_down, "w_down", desc.d_ff * desc.d_model * e, dt),
