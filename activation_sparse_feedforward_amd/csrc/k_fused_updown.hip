@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
 // and are summed in ascending range order (deterministic) before y[t] is
 // written once.
 constexpr int kTokWaves = 16;
-constexpr int kTokList = 128;  // list entries per wave per chunk
+constexpr int kTokList = kWave;  // list entries per wave and pass (one per slot)
 
 template <int NV, int EB>
 constexpr size_t token_lds_bytes() {
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
   constexpr int kRow = NV * kWave * kN;  // d_model
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int2* list = reinterpret_cast<int2*>(smem) + wave * kTokList;
+  int2* list = reinterpret_cast<int2*>(smem) + wave * kTokList;  // this wave's entries of a pass
   float* ypart = reinterpret_cast<float*>(smem + kTokWaves * kTokList * 8);  // [16][d]
   u32x4_t* xl = reinterpret_cast<u32x4_t*>(ypart + kTokWaves * kRow);       // x[t], shared by the waves
   const int64_t i_row = blockIdx.x;
@@ -475,6 +475,25 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
   const int tg = (n_t + kTokWaves - 1) / kTokWaves;
   const int b_begin = min(n_t, wave * tg), b_end = min(n_t, b_begin + tg);
 
+  // The wave's TwELL slots, tile-major (tile b_begin + s / C, slot s % C),
+  // one per lane and pass of 64: the slot's tile count, index and value are
+  // loaded together, so a pass's list takes one memory round trip, not a
+  // count load followed by index loads.  A slot holds an entry iff it is
+  // below min(count, C); entries keep ascending (tile, slot) order.
+  const int n_slots = (b_end - b_begin) * C;
+  auto slot = [&](int s, int& j, float& a) -> bool {
+    if (s >= n_slots) return false;
+    const int q = s / C, sl = s - q * C;
+    const int64_t unit = t * n_t + b_begin + q;
+    const int cnt = p.count[unit];
+    const int ix = p.idx[unit * C + sl];
+    a = load_elem<E>(p.val, unit * C + sl);
+    j = (b_begin + q) * tile_n + (ix & (tile_n - 1));
+    return sl < min(cnt, C);
+  };
+  int j_first = 0;
+  float a_first = 0.f;
+  const bool v_first = slot(lane, j_first, a_first);  // issued beside the x row
   float yf[NV][kN];
   {
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
@@ -485,21 +504,15 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
       for (int i = 0; i < kN; ++i) yf[v][i] = 0.f;
   }
   __syncthreads();
-  const int chunk_tiles = max(1, min(kWave, kTokList / C));
-  for (int b0 = b_begin; b0 < b_end; b0 += chunk_tiles) {
-    const int b = b0 + lane;
-    int cnt = 0;
-    if (lane < chunk_tiles && b < b_end) cnt = max(0, min(p.count[t * n_t + b], C));
-    const int incl = wave_incl_scan(cnt);
-    const int total = min(wave_last(incl), kTokList);
-    const int off = incl - cnt;
-    if (cnt > 0) {
-      const int64_t rec = (t * n_t + b) * C;
-      for (int s = 0; s < cnt && off + s < kTokList; ++s) {
-        const int j = b * tile_n + (p.idx[rec + s] & (tile_n - 1));
-        list[off + s] = make_int2(j, __float_as_int(load_elem<E>(p.val, rec + s)));
-      }
-    }
+  for (int s0 = 0; s0 < n_slots; s0 += kWave) {
+    int j = j_first;
+    float a = a_first;
+    const bool valid = s0 == 0 ? v_first : slot(s0 + lane, j, a);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+    const int total = static_cast<int>(__popcll(m));  // <= kTokList
+    if (valid)
+      list[__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))] =
+          make_int2(j, __float_as_int(a));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
