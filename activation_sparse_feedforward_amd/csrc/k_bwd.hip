@@ -541,10 +541,13 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
       const int incl = wave_incl_scan(cnt);
       total = min(wave_last(incl), kDxList);
       const int off = incl - cnt;
-#pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) {
+      // slots up to the largest count of the builder lanes
+      int n_s = 0;
+      while (n_s < 16 && __builtin_amdgcn_ballot_w64(cnt > n_s)) ++n_s;
+      for (int s2 = 0; s2 < n_s; ++s2) {
         if (s2 < cnt && off + s2 < kDxList) {
-          const int j = b * tile_n + (static_cast<int>((ix[s2 >> 2] >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
+          const uint32_t w = s2 < 8 ? (s2 < 4 ? ix[0] : ix[1]) : (s2 < 12 ? ix[2] : ix[3]);
+          const int j = b * tile_n + (static_cast<int>((w >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
           list[off + s2] = make_int4(j, spos + s2, kl, 0);
         }
       }

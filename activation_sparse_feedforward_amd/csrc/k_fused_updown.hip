@@ -344,10 +344,14 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
       const int incl = wave_incl_scan(cnt);
       total = min(wave_last(incl), kSyncList);
       const int off = incl - cnt;
-#pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) {
+      // slots up to the largest count of the builder lanes (a builder lane
+      // rarely holds more than a few entries of a chunk)
+      int n_s = 0;
+      while (n_s < 16 && __builtin_amdgcn_ballot_w64(cnt > n_s)) ++n_s;
+      for (int s2 = 0; s2 < n_s; ++s2) {
         if (s2 < cnt && off + s2 < kSyncList) {
-          const int j = b * tile_n + (static_cast<int>((ix[s2 >> 2] >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
+          const uint32_t w = s2 < 8 ? (s2 < 4 ? ix[0] : ix[1]) : (s2 < 12 ? ix[2] : ix[3]);
+          const int j = b * tile_n + (static_cast<int>((w >> (8 * (s2 & 3))) & 0xffu) & (tile_n - 1));
           list[off + s2] = make_int4(j, vpos + s2, kl, 0);
         }
       }
@@ -644,7 +648,9 @@ static hipError_t launch_sync_t(const FusedArgs& a, hipStream_t s) {
     const int64_t per = static_cast<int64_t>(kSyncWaves) * tpw;
     return cus <= 0 || (a.T + per - 1) / per >= cus;
   };
-  if (kMax >= 4 && fit >= 4 && fills(4)) return launch_sync_cfg<E, NV, 4, 1>(a, s);
+  if constexpr (kMax >= 4) {  // (4 rows per wave only where their accumulators fit)
+    if (fit >= 4 && fills(4)) return launch_sync_cfg<E, NV, 4, 1>(a, s);
+  }
   if (fit >= 2 && fills(2)) return launch_sync_cfg<E, NV, 2, 1>(a, s);
   return launch_sync_cfg<E, NV, 1, 1>(a, s);
 }
