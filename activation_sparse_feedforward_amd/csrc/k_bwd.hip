@@ -241,10 +241,22 @@ __global__ __launch_bounds__(256) void bwd_pos_kernel(BwdArgs p) {
 //     u = x[t].W_up^T[j], e = dy[t].W_down[j], h = a u, dh = e + l1 sign(h),
 //     du = dh a, dg = dh u
 // (a = the slot's stored ReLU value).  (dg, du) go to the slot for the dx
-// pass; dg x[t], du x[t] and h dy[t] accumulate into fp32 rows in VGPRs.  Up
-// to d_model = 2048 (bf16) two pairs are in flight per iteration.
+// pass; dg x[t], du x[t] and h dy[t] accumulate into fp32 rows in VGPRs.
+// Two waves share a SIMD, with two pairs in flight per iteration up to 4
+// 16-byte vectors per lane and one above; rows too wide for that (bf16
+// d_model >= 3072: three fp32 rows, the two weight rows and a pair's x and dy
+// pass 230 VGPRs) give the wave the SIMD to itself with two pairs in flight:
+// the same pairs in flight per CU, no spills.
 template <class E, int NV>
-__global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
+struct DwShape {
+  static constexpr int kOnePair = NV * (3 * VecB<E>::N + 16);  // VGPRs per lane, one pair in flight
+  static constexpr bool kWide = kOnePair > 230;
+  static constexpr int kWavesPerSimd = kWide ? 1 : 2;
+  static constexpr int kPairs = (NV <= 4 || kWide) ? 2 : 1;
+};
+
+template <class E, int NV>
+__global__ __launch_bounds__(4 * kWave, (DwShape<E, NV>::kWavesPerSimd)) void bwd_dw_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(4 * kWave, 2) void bwd_dw_kernel(BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < kN; ++i) ag[v][i] = au[v][i] = ad[v][i] = 0.f;
   const int beg = p.neuron_off[j], end = p.neuron_off[j + 1];
-  constexpr int kP = NV <= 4 ? 2 : 1;  // wider rows: one pair at a time, fewer spills
+  constexpr int kP = DwShape<E, NV>::kPairs;
   for (int e0 = beg; e0 < end; e0 += kP) {
     float aq[kP];
     int sq[kP];
