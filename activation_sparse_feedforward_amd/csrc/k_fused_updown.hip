@@ -244,18 +244,24 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 // index, so results are deterministic for a given row list).  Rows are dealt
 // to the waves by their entry counts (balance_rows: within each workgroup for
 // all rows, over windows of 8 workgroups for a row list), which shortens the
-// wait at every chunk barrier and keeps the workgroups in step.
+// wait at every chunk barrier and keeps the workgroups in step.  Workgroups
+// have 16 waves up to 4 16-byte vectors per lane (bf16 d_model <= 2048) and 8
+// above (bf16 d_model <= 4096), where two fp32 y rows per wave need the 256
+// VGPRs of two waves per SIMD.
 constexpr int kSyncWaves = 16;
+constexpr int kSyncWavesWide = 8;
 constexpr int kSyncList = 128;  // list entries per wave per chunk
 constexpr int kSyncChunkMax = 4;
+// a chunk's weight rows (tiles x T_n neurons x 2 rows) are at most one XCD's L2
+constexpr int64_t kSyncChunkBytes = int64_t(4) << 20;
 
-template <class E, int NV, int TPW, int kU, int kC>
-__global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(FusedArgs p) {
+template <class E, int NV, int TPW, int kU, int kC, int kW>
+__global__ __launch_bounds__(kW * kWave) void fused_updown_sync_kernel(FusedArgs p) {
   constexpr int kN = Vec<E>::N;
   constexpr int kRowVec = NV * kWave;  // 16-byte vectors per row
   extern __shared__ __align__(16) char smem[];
   u32x4_t* xl = reinterpret_cast<u32x4_t*>(smem);  // [16 waves][TPW][kRowVec]
-  int4* list_all = reinterpret_cast<int4*>(smem + kSyncWaves * TPW * kRowVec * 16);
+  int4* list_all = reinterpret_cast<int4*>(smem + kW * TPW * kRowVec * 16);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   // rows are dealt over windows of workgroups (balance_rows): only a workgroup
   // whose whole window is past the rows has none
   const int win = p.rows ? kBalanceWindow : 1;
-  if (blk / win * win * kSyncWaves * TPW >= n_rows) return;
+  if (blk / win * win * kW * TPW >= n_rows) return;
   int4* list = list_all + wave * kSyncList;
   u32x4_t* xw = xl + wave * TPW * kRowVec;
   const int d = p.d, C = kC > 0 ? kC : p.C, tile_n = p.tile_n;
@@ -271,8 +277,8 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kSyncWaves, TPW, kBalanceWindow>(p.count, p.row_total, p.rows, n_rows, n_t, blk,
-                                                (p.T + kSyncWaves * TPW - 1) / (kSyncWaves * TPW), win, wave,
+  balance_rows<kW, TPW, kBalanceWindow>(p.count, p.row_total, p.rows, n_rows, n_t, blk,
+                                        (p.T + kW * TPW - 1) / (kW * TPW), win, wave,
                                                 reinterpret_cast<int*>(list_all), src);
 
   int64_t tk[TPW];
@@ -296,9 +302,11 @@ __global__ __launch_bounds__(kSyncWaves * kWave) void fused_updown_sync_kernel(F
     }
   }
   // lanes of the list builder: lane = tile_in_chunk * TPW + token
-  // at most 4 tiles per chunk: the weight rows of a chunk (4 x 128 neurons x
-  // 2 rows x d_model x 2 B = 4 MB at d_model = 2048) then fit an XCD's L2
-  const int chunk_tiles = max(1, min(min(kWave / TPW, kSyncList / (C * TPW)), kSyncChunkMax));
+  // at most 4 tiles per chunk, and no more than an XCD's L2 holds of their
+  // weight rows (4 x 128 neurons x 2 rows x d_model x 2 B = 4 MB at d_model =
+  // 2048; 2 tiles at 4096)
+  const int l2_tiles = static_cast<int>(kSyncChunkBytes / (int64_t(tile_n) * 2 * d * E::kBytes));
+  const int chunk_tiles = max(1, min(min(kWave / TPW, kSyncList / (C * TPW)), min(kSyncChunkMax, l2_tiles)));
   // Workgroups are dealt round-robin to the 8 XCDs; each XCD's workgroups start
   // their sweep at a different chunk (and wrap around), so the XCDs do not all
   // request the same weight rows from the MALL at the same time.
@@ -593,17 +601,18 @@ static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int NV, int TPW, int EB>
+template <int NV, int TPW, int kW>
 constexpr size_t sync_lds_bytes() {
-  return static_cast<size_t>(kSyncWaves) * TPW * NV * kWave * 16 + kSyncWaves * kSyncList * 16;
+  return static_cast<size_t>(kW) * TPW * NV * kWave * 16 + kW * kSyncList * 16;
 }
 
-template <class E, int NV, int TPW, int kU>
+template <class E, int NV, int TPW, int kU, int kW>
 static hipError_t launch_sync_cfg(const FusedArgs& args, hipStream_t s) {
-  constexpr size_t lds = sync_lds_bytes<NV, TPW, E::kBytes>();
+  constexpr size_t lds = sync_lds_bytes<NV, TPW, kW>();
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   FusedArgs a = args;
   a.resident = lockstep_resident();
-  const int64_t per_block = static_cast<int64_t>(kSyncWaves) * TPW;
+  const int64_t per_block = static_cast<int64_t>(kW) * TPW;
   const int64_t blocks = (a.T + per_block - 1) / per_block;
   // one launch per generation of resident workgroups, so every generation
   // starts on a free chip, its workgroups together
@@ -614,45 +623,54 @@ static hipError_t launch_sync_cfg(const FusedArgs& args, hipStream_t s) {
     if constexpr (E::kBytes == 2) {
       if (a.C == 16) {
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 16>),
+            reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 16, kW>),
             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (attr != hipSuccess) return attr;
-        hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 16>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+        hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 16, kW>), grid, dim3(kW * kWave), lds, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         continue;
       }
     }
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 0>),
+        reinterpret_cast<const void*>(&fused_updown_sync_kernel<E, NV, TPW, kU, 0, kW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 0>), grid, dim3(kSyncWaves * kWave), lds, s, a);
+    hipLaunchKernelGGL((fused_updown_sync_kernel<E, NV, TPW, kU, 0, kW>), grid, dim3(kW * kWave), lds, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-// Tokens per wave: as many fp32 y rows as fit beside the loads in 128 VGPRs,
-// and no more than the per-chunk list holds when one tile of each token is
+// Tokens per wave: as many fp32 y rows as fit beside the loads in the VGPRs
+// of a wave (128 at 16 waves, 256 at 8) and their x rows in LDS, and no more
+// than the per-chunk list holds when one tile of each token is
 // full (TPW * C <= kSyncList, so every chunk of >= 1 tile fits), but fewer when
 // that would leave CUs without a workgroup (e.g. 8192 rows at d_model = 1024:
 // 4 tokens per wave give 128 workgroups for 256 CUs, 2 give 256).
 template <class E, int NV>
 static hipError_t launch_sync_t(const FusedArgs& a, hipStream_t s) {
-  constexpr int kMax = NV * Vec<E>::N <= 16 ? 4 : 2;
+  constexpr int kW = NV <= 4 ? kSyncWaves : kSyncWavesWide;
+  // rows per wave: their fp32 accumulators fit beside the loads, and the x rows
+  // of the workgroup fit in LDS beside the entry lists
+  constexpr int kRegMax = NV * Vec<E>::N <= 16 ? 4 : 2;
+  constexpr int kLdsMax = static_cast<int>((160 * 1024 - kW * kSyncList * 16) / (kW * NV * kWave * 16));
+  constexpr int kMax = kRegMax < kLdsMax ? kRegMax : kLdsMax;
+  static_assert(kMax >= 1, "one row per wave fits");
   const int fit = kSyncList / a.C;
   const int64_t cus = lockstep_resident();
   auto fills = [&](int tpw) {
-    const int64_t per = static_cast<int64_t>(kSyncWaves) * tpw;
+    const int64_t per = static_cast<int64_t>(kW) * tpw;
     return cus <= 0 || (a.T + per - 1) / per >= cus;
   };
-  if constexpr (kMax >= 4) {  // (4 rows per wave only where their accumulators fit)
-    if (fit >= 4 && fills(4)) return launch_sync_cfg<E, NV, 4, 1>(a, s);
+  if constexpr (kMax >= 4) {
+    if (fit >= 4 && fills(4)) return launch_sync_cfg<E, NV, 4, 1, kW>(a, s);
   }
-  if (fit >= 2 && fills(2)) return launch_sync_cfg<E, NV, 2, 1>(a, s);
-  return launch_sync_cfg<E, NV, 1, 1>(a, s);
+  if constexpr (kMax >= 2) {
+    if (fit >= 2 && fills(2)) return launch_sync_cfg<E, NV, 2, 1, kW>(a, s);
+  }
+  return launch_sync_cfg<E, NV, 1, 1, kW>(a, s);
 }
 
 template <class E, int NV>
@@ -696,6 +714,21 @@ hipError_t launch_fused_split(const FusedArgs& a, int dtype, hipStream_t s) {
 // lockstep kernel would keep fewer than T/32 workgroups busy).
 constexpr int64_t kSmallBatch = 2048;
 
+// Rows wider than 4 16-byte vectors per lane: bf16 batches of kWideSyncBatch
+// rows and more take the 8-wave lockstep kernel (from there two rows per wave
+// fill a generation of workgroups; at 2100 rows a nearly empty second
+// generation made it a third slower than a wave per token); smaller batches
+// and fp32 take a wave per token.
+constexpr int64_t kWideSyncBatch = 4096;
+
+template <class E, int NV>
+static hipError_t launch_wide_t(const FusedArgs& a, hipStream_t s) {
+  if constexpr (E::kBytes == 2) {
+    if (a.T >= kWideSyncBatch) return launch_sync_t<E, NV>(a, s);
+  }
+  return launch_fused_t<E, NV>(a, s);
+}
+
 template <class E>
 static hipError_t launch_fused_e(const FusedArgs& a, hipStream_t s) {
   const int nv = a.d / (kWave * Vec<E>::N);
@@ -720,10 +753,10 @@ static hipError_t launch_fused_e(const FusedArgs& a, hipStream_t s) {
     case 2: return launch_sync_t<E, 2>(a, s);
     case 3: return launch_sync_t<E, 3>(a, s);
     case 4: return launch_sync_t<E, 4>(a, s);
-    case 5: return launch_fused_t<E, 5>(a, s);
-    case 6: return launch_fused_t<E, 6>(a, s);
-    case 7: return launch_fused_t<E, 7>(a, s);
-    case 8: return launch_fused_t<E, 8>(a, s);
+    case 5: return launch_wide_t<E, 5>(a, s);
+    case 6: return launch_wide_t<E, 6>(a, s);
+    case 7: return launch_wide_t<E, 7>(a, s);
+    case 8: return launch_wide_t<E, 8>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,9 +5,10 @@
 // clásico?": one fused kernel gathers the weight rows of the active neurons)
 // spends its time fetching whole weight rows: per active (token, neuron) pair
 // one row of W_up^T and one of W_down, 2 * d_model bytes each at bf16.  This
-// probe moves the same rows the same way -- 16 waves per CU, every lane
-// loading 16-byte pieces of the row, two rows per step -- without any
-// arithmetic, so its rate is what the memory system gives that pattern:
+// probe moves the same rows the same way -- one workgroup per CU of 16 waves
+// (8 for rows wider than 4 KB, as the fused kernel), every lane loading
+// 16-byte pieces of the row, two rows per step -- without any arithmetic, so
+// its rate is what the memory system gives that pattern:
 //   mode 0 (random): each wave picks its rows at random from both matrices,
 //          so nearly every row comes from past L2 (the MALL holds both);
 //   mode 1 (XCD-shared): the waves of one XCD (workgroup id mod 8, the
@@ -22,7 +23,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 16;  // per workgroup (one workgroup per CU)
 
 __device__ __forceinline__ uint32_t mix(uint32_t v) {  // a 32-bit integer hash (murmur3 finaliser)
   v ^= v >> 16;
@@ -34,8 +34,8 @@ __device__ __forceinline__ uint32_t mix(uint32_t v) {  // a 32-bit integer hash 
 }
 
 // NV 16-byte pieces per lane per row (row = NV * 64 * 16 bytes); U steps of two
-// rows in flight per wave.
-template <int NV, int U>
+// rows in flight per wave; kWaves waves per workgroup.
+template <int NV, int U, int kWaves>
 __global__ __launch_bounds__(kWaves * 64) void gather_probe_kernel(const char* a, const char* b, int64_t rows,
                                                                    int steps, int shared, uint32_t* out) {
   const int lane = threadIdx.x & 63;
@@ -70,34 +70,41 @@ __global__ __launch_bounds__(kWaves * 64) void gather_probe_kernel(const char* a
   if (lane == 0) out[gw] = acc;
 }
 
-// 96 KB of (unused) LDS per workgroup keeps one workgroup, i.e. 16 waves, per
-// CU, as in the fused kernel.
+// 96 KB of (unused) LDS per workgroup keeps one workgroup per CU, as in the
+// fused kernel.
 constexpr int kPinLds = 96 * 1024;
 
-template <int NV, int U>
+template <int NV, int U, int kWaves>
 int launch_u(const char* a, const char* b, int64_t rows, int steps, int shared, int blocks, uint32_t* out,
              hipStream_t s) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_probe_kernel<NV, U>),
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_probe_kernel<NV, U, kWaves>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kPinLds) != hipSuccess)
     return 3;
-  hipLaunchKernelGGL((gather_probe_kernel<NV, U>), dim3(blocks), dim3(kWaves * 64), kPinLds, s, a, b, rows, steps,
-                     shared, out);
+  hipLaunchKernelGGL((gather_probe_kernel<NV, U, kWaves>), dim3(blocks), dim3(kWaves * 64), kPinLds, s, a, b, rows,
+                     steps, shared, out);
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
+// the deeper case keeps eight rows in flight per wave up to 4 KB rows and four
+// above (whose 8-wave workgroups have twice the registers per wave)
 template <int NV>
 int launch_nv(const char* a, const char* b, int64_t rows, int steps, int shared, int in_flight, int blocks,
               uint32_t* out, hipStream_t s) {
-  return in_flight >= 4 ? launch_u<NV, 4>(a, b, rows, steps, shared, blocks, out, s)
-                        : launch_u<NV, 1>(a, b, rows, steps, shared, blocks, out, s);
+  if constexpr (NV <= 4)
+    return in_flight >= 4 ? launch_u<NV, 4, 16>(a, b, rows, steps, shared, blocks, out, s)
+                          : launch_u<NV, 1, 16>(a, b, rows, steps, shared, blocks, out, s);
+  else
+    return in_flight >= 4 ? launch_u<NV, 2, 8>(a, b, rows, steps, shared, blocks, out, s)
+                          : launch_u<NV, 1, 8>(a, b, rows, steps, shared, blocks, out, s);
 }
 
 }  // namespace
 
-// a, b: two row-major matrices of `rows` rows of row_bytes (1024, 2048 or 4096)
-// each; out: blocks * 16 words.  steps: multiple of 4.  in_flight: 1 (two rows
-// per wave in flight, as the fused kernel) or 4 (eight rows).  Returns 0 on
-// success, non-zero for a bad argument or a failed launch.
+// a, b: two row-major matrices of `rows` rows of row_bytes (1024, 2048, 4096,
+// 5120, 6144, 7168 or 8192) each; out: blocks * 16 words.  steps: multiple of
+// 4.  in_flight: 1 (two rows per wave in flight, as the fused kernel) or 4
+// (eight rows; four for rows wider than 4 KB).  Returns 0 on success, non-zero
+// for a bad argument or a failed launch.
 extern "C" int twell_probe_gather(const void* a, const void* b, int64_t rows, int row_bytes, int steps, int shared,
                                   int in_flight, int blocks, uint32_t* out, void* stream) {
   if (!a || !b || !out || rows <= 0 || rows > (int64_t(1) << 31) || steps <= 0 || steps % 4 || blocks <= 0)
@@ -109,6 +116,10 @@ extern "C" int twell_probe_gather(const void* a, const void* b, int64_t rows, in
     case 1024: return launch_nv<1>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
     case 2048: return launch_nv<2>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
     case 4096: return launch_nv<4>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
+    case 5120: return launch_nv<5>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
+    case 6144: return launch_nv<6>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
+    case 7168: return launch_nv<7>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
+    case 8192: return launch_nv<8>(pa, pb, rows, steps, shared, in_flight, blocks, out, s);
   }
   return 2;
 }

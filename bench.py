@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload id (default: the 2B-class inference shape)")
     ap.add_argument("--rho", type=float, default=None, help="override the gate density (sweep workload)")
     ap.add_argument("--T", type=int, default=None, help="override the token count")
+    ap.add_argument("--d-model", type=int, default=None,
+                    help="override d_model (e.g. 4096 with --d-ff 11008: a Llama-7B-shaped layer)")
     ap.add_argument("--d-ff", type=int, default=None,
                     help="override d_ff (e.g. 1024: one GPU's share of the 2B-class FFN split 8 ways over neurons)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
@@ -193,9 +195,10 @@ def cpu_baseline(inp, budget_s: float, tile_n: int, slots: int, dtype: str):
 
 def gather_ceiling(wu, wd, stream, steps=256, reps=5):
     """Rate at which the memory system serves the fused kernel's access pattern
-    (16 waves per CU, whole weight rows, two rows per step) with no arithmetic:
-    random rows (mostly past L2) and rows shared by every wave of an XCD
-    (mostly from L2), each with two and with eight rows in flight per wave.
+    (one workgroup per CU of 16 waves, 8 for rows wider than 4 KB; whole weight
+    rows, two rows per step) with no arithmetic: random rows (mostly past L2)
+    and rows shared by every wave of an XCD (mostly from L2), each with two and
+    with eight rows in flight per wave (four for rows wider than 4 KB).
     Returns GB/s per case and the ceilings (best of the two depths)."""
     import ctypes
     import numpy as np
@@ -209,6 +212,7 @@ def gather_ceiling(wu, wd, stream, steps=256, reps=5):
     lib.twell_probe_gather.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, P, P]
     rows, row_bytes = wu.shape[0], wu.shape[1] * wu.element_size()
+    waves, deep = (16, 8) if row_bytes <= 4096 else (8, 4)  # per workgroup; rows in flight per wave
     blocks = torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(blocks * 16, dtype=torch.int32, device="cuda")
     st = stream.cuda_stream
@@ -232,11 +236,13 @@ def gather_ceiling(wu, wd, stream, steps=256, reps=5):
                 e1.record(stream)
                 torch.cuda.synchronize()
                 ts.append(e0.elapsed_time(e1))
-            nbytes = blocks * 16 * steps * 2 * row_bytes
-            res[f"{name}_rows_{2 * depth}_in_flight_gbs"] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
-    res["random_ceiling_gbs"] = max(res["random_rows_2_in_flight_gbs"], res["random_rows_8_in_flight_gbs"])
-    res["xcd_shared_ceiling_gbs"] = max(res["xcd_shared_rows_2_in_flight_gbs"], res["xcd_shared_rows_8_in_flight_gbs"])
-    res["bytes_per_launch"] = blocks * 16 * steps * 2 * row_bytes
+            nbytes = blocks * waves * steps * 2 * row_bytes
+            res[f"{name}_rows_{2 if depth == 1 else deep}_in_flight_gbs"] = round(
+                nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    res["random_ceiling_gbs"] = max(res["random_rows_2_in_flight_gbs"], res[f"random_rows_{deep}_in_flight_gbs"])
+    res["xcd_shared_ceiling_gbs"] = max(res["xcd_shared_rows_2_in_flight_gbs"],
+                                        res[f"xcd_shared_rows_{deep}_in_flight_gbs"])
+    res["bytes_per_launch"] = blocks * waves * steps * 2 * row_bytes
     return res
 
 
@@ -596,8 +602,8 @@ def main():
         print(json.dumps({"sweep": "llama2B_ffn_sweep_T16384_d2048_F8192", "steps": args.steps,
                           "warmup": args.warmup, "points": density_sweep(T, W, args)}), flush=True)
         return
-    w = W.workload(args.config, T=args.T, rho=args.rho, d_ff=args.d_ff)
-    overridden = args.T is not None or args.rho is not None or args.d_ff is not None
+    w = W.workload(args.config, T=args.T, rho=args.rho, d_model=args.d_model, d_ff=args.d_ff)
+    overridden = args.T is not None or args.rho is not None or args.d_ff is not None or args.d_model is not None
     if args.mfma_ceiling:
         st = torch.cuda.current_stream()
         print(json.dumps({"mfma_ceiling": mfma_ceiling(st),
@@ -612,7 +618,7 @@ def main():
         print(json.dumps({"gather_ceiling": gather_ceiling(wu_p, wd_p, torch.cuda.current_stream()),
                           "rows": "W_up^T and W_down of " + w.name}), flush=True)
         return
-    wname = w.name if not overridden else f"{w.name}@T{w.T}_F{w.d_ff}_rho{w.rho}"
+    wname = w.name if not overridden else f"{w.name}@T{w.T}_d{w.d_model}_F{w.d_ff}_rho{w.rho}"
     inp = W.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 

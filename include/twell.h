@@ -144,19 +144,23 @@ twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* 
  * intermediate never written to memory.
  * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down
  * projections together; the intermediate never reaches global memory.]
- * Dispatches: rows wider than 2048 elements (bf16; 1024 in fp32) take a
- * one-wave-per-row kernel and batches below 2048 rows a one-workgroup-per-row
- * kernel, each in ONE dispatch.  Batches of 2048 rows and more take the lockstep kernel
- * (workgroups of 16 waves that sweep the neuron tiles together, each wave
- * holding R rows: as many as its registers and per-wave list allow -- 2 at
- * d_model = 2048, 4 at d_model <= 1024 when C <= 32 -- but fewer while that
+ * Dispatches, by batch size T and row width d_model: below 2048 rows a
+ * one-workgroup-per-row kernel (d_model <= 2048) or a one-wave-per-row kernel
+ * (wider bf16 rows), in ONE dispatch; the one-wave-per-row kernel also for
+ * fp32 rows wider than 1024 and for bf16 rows wider than 2048 below 4096
+ * rows.  All other batches take the lockstep kernel (workgroups of W waves --
+ * 16, or 8 for bf16 rows wider than 2048 -- that sweep the neuron tiles
+ * together, each wave holding R rows: as many as its registers, the
+ * workgroup's LDS and the per-wave list allow -- 2 at d_model = 2048 and at
+ * 2560 .. 4096, 4 at d_model <= 1024 when C <= 32 -- but fewer while that
  * would leave CUs without a workgroup), dispatched once per generation of
  * workgroups the device runs at once (one per CU), on disjoint row blocks:
- * ceil(ceil(T / (16 R)) / CUs) dispatches of the same kernel, e.g. 2 at
- * T = 16384, d_model = 2048 (R = 2) and 1 at T = 8192, d_model = 1024 (R = 2)
- * on a 256-CU MI355X.  Every row is computed start to finish by one workgroup
- * of one dispatch; a workgroup deals its rows to its waves by their entry
- * counts (a row's result does not depend on the wave).
+ * ceil(ceil(T / (W R)) / CUs) dispatches of the same kernel, e.g. 2 at
+ * T = 16384, d_model = 2048 (W = 16, R = 2), 1 at T = 8192, d_model = 1024
+ * (R = 2) and 4 at T = 16384, d_model = 4096 (W = 8, R = 2) on a 256-CU
+ * MI355X.  Every row is computed start to finish by one workgroup of one
+ * dispatch; a workgroup deals its rows to its waves by their entry counts (a
+ * row's result does not depend on the wave).
  * Bits: each row's tiles are summed starting at a chunk that depends on its
  * workgroup's index and generation, hence on the device's CU count; y is
  * bitwise reproducible on one device (and on devices with the same CU count),

@@ -234,6 +234,22 @@ def test_lockstep_three_generations_sampled():
     _check_case(w, rows=np.array(sorted(rows)), label="three generations")
 
 
+@pytest.mark.parametrize("T_,d,F", [(4096, 4096, 11008), (8192, 3072, 8192)], ids=["d4096 one generation",
+                                                                                "d3072 two generations"])
+def test_lockstep_wide_rows_sampled(T_, d, F):
+    """bf16 rows wider than 2048 from 4096 tokens on take the 8-wave lockstep
+    kernel (two rows per wave, chunks of at most 2 tiles at d_model = 4096):
+    TwELL byte for byte on all rows, the gate and y on sampled rows, and a
+    second call gives the same bits."""
+    w = W.workload(3, T=T_, d_model=d, d_ff=F)
+    r, _ = _check_case(w, rows=_sample_rows(w.T, d), label="wide lockstep")
+    y2 = guarded(tuple(r["y"].shape), r["y"].dtype)
+    T.twell_ffn_fwd(desc_for(w), r["x"], r["act"], r["wu"], r["wd"], y2)
+    torch.cuda.synchronize()
+    check_guards(y2)
+    assert torch.equal(r["y"].view(torch.int16), y2.view(torch.int16))
+
+
 def test_dense_ffn_full_size_sampled():
     """The dense FFN in the configuration the benchmark times (2B-class shape,
     T=16384), checked on sampled rows against the float64 dense FFN."""

@@ -133,6 +133,15 @@ def test_hybrid_lockstep_four_rows_per_wave_sampled():
     run_hybrid(w, 1024, rows=rows, label="lognormal d=1024")
 
 
+def test_hybrid_wide_rows_lockstep_sampled():
+    # d_model = 4096 at 4096 rows: the light rows take the 8-wave lockstep
+    # kernel, dealt over windows of 8 workgroups by their totals
+    w = W.workload(4, T=4096, d_model=4096, d_ff=11008)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(w.T - 128, w.T), rng.choice(w.T, 192, replace=False)]))
+    run_hybrid(w, 256, rows=rows, label="lognormal d=4096")
+
+
 def test_hybrid_deterministic_lockstep():
     """A batch large enough for the lockstep fused kernel (whose chunk order
     depends on the workgroup), with heavy and dense rows: two calls give the
