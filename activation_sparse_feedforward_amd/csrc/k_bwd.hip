@@ -467,19 +467,27 @@ __global__ __launch_bounds__(kTokWaves * kWave, 2) void bwd_ell_dx_kernel(BwdArg
   }
 }
 
-// Light rows in lockstep: 16 waves of TPW rows each, fp32 dx rows in VGPRs.
-// Every chunk of tiles starts with a workgroup barrier, so the resident
-// workgroups sweep the neurons in roughly the same order and the two weight
-// rows of each pair are reused from L2; each XCD's workgroups (dealt
-// round-robin) start at a different chunk and wrap around.
+// Light rows in lockstep: kW waves of TPW rows each, fp32 dx rows in VGPRs
+// (16 waves up to bf16 d_model = 2048; 8 above, whose two rows per wave need
+// the 256 VGPRs of two waves per SIMD).  Every chunk of tiles starts with a
+// workgroup barrier, so the resident workgroups sweep the neurons in roughly
+// the same order and the two weight rows of each pair are reused from L2;
+// each XCD's workgroups (dealt round-robin) start at a different chunk and
+// wrap around.
 constexpr int kDxWaves = 16;
+constexpr int kDxWavesWide = 8;
+constexpr int64_t kDxWideBatch = 4096;  // rows from which wider rows take the lockstep dx pass
 constexpr int kDxList = 128;      // {j, slot, row} entries per wave per chunk
-constexpr int kDxChunkMax = 4;    // 4 tiles x 128 neurons x 2 rows x 4 KB = 4 MB, an XCD's L2
+constexpr int kDxChunkMax = 4;
+// a chunk's weight rows at most one XCD's L2: 4 tiles x 128 neurons x 2 rows x
+// 4 KB = 4 MB at d_model = 2048, 2 tiles at 4096
+constexpr int64_t kDxChunkBytes = int64_t(4) << 20;
 
-constexpr size_t bwd_dx_sync_lds_bytes() { return static_cast<size_t>(kDxWaves) * kDxList * 16; }
+template <int kW>
+constexpr size_t bwd_dx_sync_lds_bytes() { return static_cast<size_t>(kW) * kDxList * 16; }
 
-template <class E, int NV, int TPW, int kC>
-__global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdArgs p) {
+template <class E, int NV, int TPW, int kC, int kW>
+__global__ __launch_bounds__(kW * kWave) void bwd_ell_dx_sync_kernel(BwdArgs p) {
   constexpr int kN = VecB<E>::N;
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63;
@@ -491,13 +499,13 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   const int64_t blk = p.blk0 + blockIdx.x;  // row block of this workgroup
   // rows are dealt over windows of workgroups (balance_rows): only a workgroup
   // whose whole window is past the rows has none
-  if (blk / kBalanceWindow * kBalanceWindow * kDxWaves * TPW >= n_rows) return;
+  if (blk / kBalanceWindow * kBalanceWindow * kW * TPW >= n_rows) return;
   int64_t src[TPW];
   // the ranking's scratch sits in the entry lists, first written after the
   // barrier that opens the first chunk
-  balance_rows<kDxWaves, TPW, kBalanceWindow>(p.count, p.row_total, p.light_rows, n_rows, n_t, blk,
-                                              (p.T + kDxWaves * TPW - 1) / (kDxWaves * TPW), kBalanceWindow, wave,
-                                              reinterpret_cast<int*>(smem), src);
+  balance_rows<kW, TPW, kBalanceWindow>(p.count, p.row_total, p.light_rows, n_rows, n_t, blk,
+                                        (p.T + kW * TPW - 1) / (kW * TPW), kBalanceWindow, wave,
+                                        reinterpret_cast<int*>(smem), src);
   int64_t tk[TPW];
   bool act[TPW];
   float dxf[TPW][NV][kN];
@@ -512,7 +520,8 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
       for (int i = 0; i < kN; ++i) dxf[k][v][i] = 0.f;
   }
   // list builder lanes: lane = tile_in_chunk * TPW + row
-  const int chunk_tiles = max(1, min(min(kWave / TPW, kDxList / (C * TPW)), kDxChunkMax));
+  const int l2_tiles = static_cast<int>(kDxChunkBytes / (int64_t(tile_n) * 2 * d * E::kBytes));
+  const int chunk_tiles = max(1, min(min(kWave / TPW, kDxList / (C * TPW)), min(kDxChunkMax, l2_tiles)));
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
   // a later generation starts one chunk earlier than the one before it, on the
   // chunk its XCD's previous generation swept last (still in L2)
@@ -618,39 +627,41 @@ __global__ __launch_bounds__(kDxWaves * kWave) void bwd_ell_dx_sync_kernel(BwdAr
   }
 }
 
-template <class E, int NV, int TPW, int kC>
+template <class E, int NV, int TPW, int kC, int kW>
 static hipError_t launch_bwd_dx_sync_c(const BwdArgs& args, hipStream_t s) {
   BwdArgs a = args;
   a.resident = lockstep_resident();
-  constexpr size_t lds = bwd_dx_sync_lds_bytes();
+  constexpr size_t lds = bwd_dx_sync_lds_bytes<kW>();
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_ell_dx_sync_kernel<E, NV, TPW, kC, kW>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  constexpr int64_t per_block = static_cast<int64_t>(kDxWaves) * TPW;
+  constexpr int64_t per_block = static_cast<int64_t>(kW) * TPW;
   const int64_t blocks = (a.T + per_block - 1) / per_block;
   // one launch per generation of resident workgroups (as the forward's lockstep kernel)
   const int64_t step = a.resident > 0 ? a.resident : blocks;
   for (int64_t b0 = 0; b0 < blocks; b0 += step) {
     a.blk0 = b0;
-    hipLaunchKernelGGL((bwd_ell_dx_sync_kernel<E, NV, TPW, kC>),
-                       dim3(static_cast<unsigned>(blocks - b0 < step ? blocks - b0 : step)), dim3(kDxWaves * kWave), lds,
-                       s, a);
+    hipLaunchKernelGGL((bwd_ell_dx_sync_kernel<E, NV, TPW, kC, kW>),
+                       dim3(static_cast<unsigned>(blocks - b0 < step ? blocks - b0 : step)), dim3(kW * kWave), lds, s,
+                       a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 // Rows per wave: two fp32 dx rows beside one pair's two weight rows fit the
-// 128 VGPRs of a 16-wave workgroup up to d_model = 2048 (bf16) / 1024 (fp32);
-// TPW * C <= kDxList, so every chunk of >= 1 tile fits the list.
+// 128 VGPRs of a 16-wave workgroup up to d_model = 2048 (bf16) / 1024 (fp32),
+// and the 256 of an 8-wave workgroup up to bf16 d_model = 4096; TPW * C <=
+// kDxList, so every chunk of >= 1 tile fits the list.
 template <class E, int NV>
 static hipError_t launch_bwd_dx_sync(const BwdArgs& a, hipStream_t s) {
-  constexpr bool two = NV * VecB<E>::N <= 32;
+  constexpr int kW = NV * VecB<E>::N <= 32 ? kDxWaves : kDxWavesWide;
+  constexpr bool two = NV * VecB<E>::N <= 32 || kW == kDxWavesWide;
   if constexpr (E::kBytes == 2)
-    if (a.C == 16) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 16>(a, s);
-  if (two && 2 * a.C <= kDxList) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 0>(a, s);
-  return launch_bwd_dx_sync_c<E, NV, 1, 0>(a, s);
+    if (a.C == 16) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 16, kW>(a, s);
+  if (two && 2 * a.C <= kDxList) return launch_bwd_dx_sync_c<E, NV, two ? 2 : 1, 0, kW>(a, s);
+  return launch_bwd_dx_sync_c<E, NV, 1, 0, kW>(a, s);
 }
 
 // ---------------------------------------------------------------- row totals (for the split)
@@ -698,42 +709,44 @@ static hipError_t launch_bwd_sparse_t(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dw_kernel<E, NV>), dim3(static_cast<unsigned>((a.F + 3) / 4)), dim3(4 * kWave), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!nblk) return hipSuccess;
-  if constexpr (NV <= 4) {
-    // light rows in lockstep, heavy rows cut into tile ranges
-    const unsigned tblk = static_cast<unsigned>((a.T + 255) / 256);
-    hipLaunchKernelGGL(bwd_totals_kernel, dim3(tblk), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    RouteArgs r{};
-    r.T = a.T;
-    r.C = a.C;
-    r.ell_rows = const_cast<int32_t*>(a.ell_rows);
-    r.n_rows = const_cast<int32_t*>(a.n_rows);
-    r.row_total = a.row_total;
-    r.block_total = a.block_total;
-    r.light_rows = a.light_rows;
-    r.heavy_rows = a.heavy_rows;
-    r.split_n = a.split_n;
-    r.block_heavy = a.block_heavy;
-    r.heavy_cap = a.heavy_cap;
-    if ((e = launch_route_split(r, s)) != hipSuccess) return e;
-    if ((e = launch_bwd_dx_sync<E, NV>(a, s)) != hipSuccess) return e;
-    const int64_t units = a.heavy_cap * a.groups;
-    if (units > 0) {
-      hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, true>),
-                         dim3(static_cast<unsigned>((units + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0,
-                         s, a);
+  // light rows in lockstep, heavy rows cut into tile ranges; bf16 rows wider
+  // than 2048 only from kDxWideBatch rows on (below, the 8-wave lockstep
+  // workgroups leave most CUs idle), fp32 rows wider than 1024 never
+  if constexpr (NV <= 4 || E::kBytes == 2) {
+    if (NV <= 4 || a.T >= kDxWideBatch) {
+      const unsigned tblk = static_cast<unsigned>((a.T + 255) / 256);
+      hipLaunchKernelGGL(bwd_totals_kernel, dim3(tblk), dim3(256), 0, s, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      e = launch_splitk_reduce(a.dx_hpart, a.groups, a.heavy_cap, a.split_n + 1, a.heavy_rows, a.dx, a.d,
-                               E::kBytes == 2 ? 1 : 0, s);
-      if (e != hipSuccess) return e;
+      RouteArgs r{};
+      r.T = a.T;
+      r.C = a.C;
+      r.ell_rows = const_cast<int32_t*>(a.ell_rows);
+      r.n_rows = const_cast<int32_t*>(a.n_rows);
+      r.row_total = a.row_total;
+      r.block_total = a.block_total;
+      r.light_rows = a.light_rows;
+      r.heavy_rows = a.heavy_rows;
+      r.split_n = a.split_n;
+      r.block_heavy = a.block_heavy;
+      r.heavy_cap = a.heavy_cap;
+      if ((e = launch_route_split(r, s)) != hipSuccess) return e;
+      if ((e = launch_bwd_dx_sync<E, NV>(a, s)) != hipSuccess) return e;
+      const int64_t units = a.heavy_cap * a.groups;
+      if (units > 0) {
+        hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, true>),
+                           dim3(static_cast<unsigned>((units + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0,
+                           s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        e = launch_splitk_reduce(a.dx_hpart, a.groups, a.heavy_cap, a.split_n + 1, a.heavy_rows, a.dx, a.d,
+                                 E::kBytes == 2 ? 1 : 0, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
-  } else {
-    hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, false>),
-                       dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)), dim3(kTokWaves * kWave), 0, s,
-                       a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipSuccess;
+  hipLaunchKernelGGL((bwd_ell_dx_kernel<E, NV, false>), dim3(static_cast<unsigned>((a.T + kTokWaves - 1) / kTokWaves)),
+                     dim3(kTokWaves * kWave), 0, s, a);
+  return hipGetLastError();
 }
 
 template <class E>

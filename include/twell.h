@@ -213,7 +213,10 @@ twell_status twell_ffn_fwd_hybrid(const twell_desc* d, const void* x, const void
  * terms in ascending token order, plus the dense rows' GEMM result (bitwise
  * the same on any device).  dx of the ELL rows comes from
  * a lockstep kernel dispatched once per generation of resident workgroups like
- * twell_ffn_fwd's, with the same dependence of its bits on the CU count.
+ * twell_ffn_fwd's (16 waves per workgroup, 8 for bf16 rows wider than 2048,
+ * which take it from 4096 rows on and one wave per row below; fp32 rows wider
+ * than 1024 always one wave per row), with the same dependence of its bits on
+ * the CU count.
  * ws: twell_sizes(d, route->max_dense_rows).ws_bwd bytes. */
 twell_status twell_ffn_bwd(const twell_desc* d, const void* x, twell_act act, const twell_route* route,
                            const void* w_gate_t, const void* w_up_t, const void* w_down, const void* dy,

@@ -93,11 +93,19 @@ def test_backward_fp32():
 
 
 def test_backward_wide_rows():
-    """d_model = 4096 (bf16), the widest rows the library takes: the dx pass
-    then runs one wave per ELL row instead of the lockstep workgroups."""
+    """d_model = 4096 (bf16), the widest rows the library takes, at 160 rows:
+    the dx pass runs one wave per ELL row (the lockstep workgroups take wide
+    rows from 4096 rows on)."""
     import dataclasses
     w = dataclasses.replace(W.workload(4, T=160), d_model=4096)
     run_bwd(w, 64, label="d_model=4096")
+
+
+def test_backward_wide_rows_lockstep():
+    """d_model = 4096 at 4096 lognormal rows: the light rows' dx in the 8-wave
+    lockstep workgroups (two rows per wave), the heavy rows cut into tile
+    ranges, all outputs against the oracle."""
+    run_bwd(W.workload(4, T=4096, d_model=4096, d_ff=8192), 256, label="d_model=4096 lockstep")
 
 
 def test_backward_wide_ff():
