@@ -453,38 +453,40 @@ __global__ __launch_bounds__(kW * kWave) void fused_updown_sync_kernel(FusedArgs
   }
 }
 
-// Small-batch variant (few tokens, d_model up to 2048): one workgroup of 16
-// waves per token, the waves splitting the token's tiles into 16 ranges, so a
-// batch of T tokens keeps T workgroups busy instead of T/32.  Each wave walks
-// its range like fused_updown_kernel; the 16 fp32 partial rows meet in LDS
-// and are summed in ascending range order (deterministic) before y[t] is
-// written once.
+// Small-batch variant (few tokens): one workgroup of kW waves per token (16;
+// 8 for bf16 rows wider than 2048, whose fp32 partial row needs the 256 VGPRs
+// of two waves per SIMD), the waves splitting the token's tiles into kW
+// ranges, so a batch of T tokens keeps T workgroups busy instead of T/32.
+// Each wave walks its range like fused_updown_kernel; the kW fp32 partial rows
+// meet in LDS and are summed in ascending range order (deterministic) before
+// y[t] is written once.
 constexpr int kTokWaves = 16;
+constexpr int kTokWavesWide = 8;  // bf16 rows wider than 2048: 256 VGPRs per wave for the fp32 partial row
 constexpr int kTokList = kWave;  // list entries per wave and pass (one per slot)
 
-template <int NV, int EB>
+template <int NV, int EB, int kW>
 constexpr size_t token_lds_bytes() {
-  return static_cast<size_t>(kTokWaves) * kTokList * 8 + static_cast<size_t>(kTokWaves) * NV * kWave * (16 / EB) * 4 +
+  return static_cast<size_t>(kW) * kTokList * 8 + static_cast<size_t>(kW) * NV * kWave * (16 / EB) * 4 +
          static_cast<size_t>(NV) * kWave * 16;
 }
 
-template <class E, int NV>
-__global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(FusedArgs p) {
+template <class E, int NV, int kW>
+__global__ __launch_bounds__(kW * kWave) void fused_updown_token_kernel(FusedArgs p) {
   constexpr int kN = Vec<E>::N;
   constexpr int kU = NV <= 2 ? 4 : (NV <= 4 ? 2 : 1);
   constexpr int kRow = NV * kWave * kN;  // d_model
   extern __shared__ __align__(16) char smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int2* list = reinterpret_cast<int2*>(smem) + wave * kTokList;  // this wave's entries of a pass
-  float* ypart = reinterpret_cast<float*>(smem + kTokWaves * kTokList * 8);  // [16][d]
-  u32x4_t* xl = reinterpret_cast<u32x4_t*>(ypart + kTokWaves * kRow);       // x[t], shared by the waves
+  float* ypart = reinterpret_cast<float*>(smem + kW * kTokList * 8);  // [kW][d]
+  u32x4_t* xl = reinterpret_cast<u32x4_t*>(ypart + kW * kRow);       // x[t], shared by the waves
   const int64_t i_row = blockIdx.x;
   const int64_t n_rows = p.n_rows_dev ? static_cast<int64_t>(*p.n_rows_dev) : p.T;
   if (i_row >= n_rows) return;  // uniform over the workgroup, before any barrier
   const int64_t t = p.rows ? static_cast<int64_t>(p.rows[i_row]) : i_row;
   const int d = p.d, C = p.C, tile_n = p.tile_n;
   const int n_t = p.F / tile_n;
-  const int tg = (n_t + kTokWaves - 1) / kTokWaves;
+  const int tg = (n_t + kW - 1) / kW;
   const int b_begin = min(n_t, wave * tg), b_end = min(n_t, b_begin + tg);
 
   // The wave's TwELL slots, tile-major (tile b_begin + s / C, slot s % C),
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
   float yf[NV][kN];
   {
     const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.x) + t * d * E::kBytes);
-    for (int v = threadIdx.x; v < NV * kWave; v += kTokWaves * kWave) xl[v] = xr[v];
+    for (int v = threadIdx.x; v < NV * kWave; v += kW * kWave) xl[v] = xr[v];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
 #pragma unroll
@@ -581,23 +583,25 @@ __global__ __launch_bounds__(kTokWaves * kWave) void fused_updown_token_kernel(F
       *reinterpret_cast<float4*>(mine + (v * kWave + lane) * kN + i) =
           make_float4(yf[v][i], yf[v][i + 1], yf[v][i + 2], yf[v][i + 3]);
   __syncthreads();
-  for (int e = threadIdx.x; e < kRow; e += kTokWaves * kWave) {
+  for (int e = threadIdx.x; e < kRow; e += kW * kWave) {
     float acc = ypart[e];
 #pragma unroll
-    for (int w = 1; w < kTokWaves; ++w) acc += ypart[w * kRow + e];
+    for (int w = 1; w < kW; ++w) acc += ypart[w * kRow + e];
     store_bits<E>(p.y, t * d + e, round_store<E>(acc).bits);
   }
 }
 
 template <class E, int NV>
 static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
-  constexpr size_t lds = token_lds_bytes<NV, E::kBytes>();
+  constexpr int kW = NV * Vec<E>::N <= 32 ? kTokWaves : kTokWavesWide;
+  constexpr size_t lds = token_lds_bytes<NV, E::kBytes, kW>();
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fused_updown_token_kernel<E, NV>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&fused_updown_token_kernel<E, NV, kW>), hipFuncAttributeMaxDynamicSharedMemorySize,
       static_cast<int>(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fused_updown_token_kernel<E, NV>), dim3(static_cast<unsigned>(a.T)), dim3(kTokWaves * kWave),
-                     lds, s, a);
+  hipLaunchKernelGGL((fused_updown_token_kernel<E, NV, kW>), dim3(static_cast<unsigned>(a.T)), dim3(kW * kWave), lds, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -732,20 +736,17 @@ static hipError_t launch_wide_t(const FusedArgs& a, hipStream_t s) {
 template <class E>
 static hipError_t launch_fused_e(const FusedArgs& a, hipStream_t s) {
   const int nv = a.d / (kWave * Vec<E>::N);
-  if (a.T < kSmallBatch && a.d <= 2048) {
-    switch (nv) {  // d_model <= 2048: NV <= 4 in bf16, <= 8 in fp32
+  if (a.T < kSmallBatch) {
+    switch (nv) {  // NV <= 8: d_model <= 4096 in bf16 (8 waves above 2048), <= 2048 in fp32
       case 1: return launch_token_t<E, 1>(a, s);
       case 2: return launch_token_t<E, 2>(a, s);
       case 3: return launch_token_t<E, 3>(a, s);
       case 4: return launch_token_t<E, 4>(a, s);
-      default:
-        if constexpr (E::kBytes == 4) {
-          if (nv == 5) return launch_token_t<E, 5>(a, s);
-          if (nv == 6) return launch_token_t<E, 6>(a, s);
-          if (nv == 7) return launch_token_t<E, 7>(a, s);
-          if (nv == 8) return launch_token_t<E, 8>(a, s);
-        }
-        return hipErrorInvalidValue;
+      case 5: return launch_token_t<E, 5>(a, s);
+      case 6: return launch_token_t<E, 6>(a, s);
+      case 7: return launch_token_t<E, 7>(a, s);
+      case 8: return launch_token_t<E, 8>(a, s);
+      default: return hipErrorInvalidValue;
     }
   }
   switch (nv) {

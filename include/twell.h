@@ -145,10 +145,10 @@ twell_status twell_pack_classic(const twell_desc* d, const void* x, const void* 
  * [P2 §TwELL-vs-ELL: one fused kernel reads TwELL and runs the up and down
  * projections together; the intermediate never reaches global memory.]
  * Dispatches, by batch size T and row width d_model: below 2048 rows a
- * one-workgroup-per-row kernel (d_model <= 2048) or a one-wave-per-row kernel
- * (wider bf16 rows), in ONE dispatch; the one-wave-per-row kernel also for
- * fp32 rows wider than 1024 and for bf16 rows wider than 2048 below 4096
- * rows.  All other batches take the lockstep kernel (workgroups of W waves --
+ * one-workgroup-per-row kernel (16 waves; 8 for bf16 rows wider than 2048), in
+ * ONE dispatch; a one-wave-per-row kernel, in ONE dispatch, for fp32 rows
+ * wider than 1024 and for bf16 rows wider than 2048 from 2048 to 4095 rows.
+ * All other batches take the lockstep kernel (workgroups of W waves --
  * 16, or 8 for bf16 rows wider than 2048 -- that sweep the neuron tiles
  * together, each wave holding R rows: as many as its registers, the
  * workgroup's LDS and the per-wave list allow -- 2 at d_model = 2048 and at

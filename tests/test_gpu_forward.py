@@ -119,6 +119,9 @@ CASES = [
     ("c4 lognormal tail", W.workload(4, T=520)),
     ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
     ("wide d_ff=16384", W.workload(4, T=300, d_model=512, d_ff=16384)),
+    # below 2048 rows, bf16 rows wider than 2048 take the 8-wave per-token workgroups
+    ("wide rows d=4096 T=16", W.workload(3, T=16, d_model=4096, d_ff=11008)),
+    ("wide rows d=3072 T=300", W.workload(5, T=300, d_model=3072, d_ff=8192, rho=0.02)),
     # batches of 2048+ tokens take the lockstep fused kernel (smaller ones the per-token kernel)
     ("lockstep ragged T=2049", W.workload(2, T=2049)),
     ("lockstep C=T_n T=2080", dataclasses.replace(W.workload(2, T=2080, rho=0.3), slots=128)),

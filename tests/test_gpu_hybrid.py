@@ -142,6 +142,11 @@ def test_hybrid_wide_rows_lockstep_sampled():
     run_hybrid(w, 256, rows=rows, label="lognormal d=4096")
 
 
+def test_hybrid_wide_rows_per_token():
+    # d_model = 4096 below 2048 rows: the light rows take the 8-wave per-token workgroups
+    run_hybrid(W.workload(4, T=300, d_model=4096, d_ff=8192), 64, label="lognormal d=4096 T=300")
+
+
 def test_hybrid_deterministic_lockstep():
     """A batch large enough for the lockstep fused kernel (whose chunk order
     depends on the workgroup), with heavy and dense rows: two calls give the
