@@ -535,26 +535,28 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Small batches (T <= 64, bf16, T_n = 128): the work is reading W_gate once, so
-// the tiling is turned around.  One workgroup per TwELL tile (128 neurons); the
-// neurons are the MFMA's M side and the tokens its N side.  With only F/128
+// Small and mid-size batches (T <= kMidT, bf16, T_n = 128): the work is
+// mostly reading W_gate, so the tiling is turned around.  One workgroup per
+// TwELL tile (128 neurons) and block of up to 128 tokens (one block up to 64
+// tokens); the neurons are the MFMA's M side and the tokens its N side.  With only F/128
 // workgroups each CU must stream its tile's 128 weight rows fast, and what
 // limits it is the trip through LDS, not HBM: coalesced 16-byte register loads
 // (8 rows x 128 bytes per wave instruction; loads in MFMA-fragment order touch
 // two to four times as many cache lines per instruction and stream far slower)
 // fetch each 128-byte K slice of the 128 weight rows and of XR token rows (XR =
-// 16, 32 or 64: the batch rounded up) kSmallAhead slices ahead, and a slice is
+// 16, 32, 64 or 128: the block rounded up) kSmallAhead slices ahead, and a slice is
 // stored into a two-slice LDS ring just before its one barrier.  Eight waves
 // form two groups of four; in a group, wave w takes neurons 32w .. 32w + 31,
 // and the two groups take alternate k-steps of every slice, so each MFMA chain
 // is half as long; group 1 parks its partial sums in LDS after the loop and
 // group 0 adds them (a fixed order).  Up to 16 tokens the MFMA is 16x16x32
-// (16 neurons x 16 tokens), above that 32x32x16 (one 32-token block, two
-// above 32 tokens).  ReLU(g), rounded to bf16, is then staged in LDS as
+// (16 neurons x 16 tokens), above that 32x32x16 on 32-token blocks (those
+// past the batch are skipped).  ReLU(g), rounded to bf16, is then staged in LDS as
 // [token][128] and each wave packs every 8th token: lane l holds columns 2l,
 // 2l + 1, and ballots give the slots in ascending column order.  Same stored
 // values and format as the large-batch kernels.
-constexpr int kSmallT = 64;
+constexpr int kSmallT = 64;   // one token block up to here
+constexpr int kMidT = 512;    // blocks of 128 tokens up to here (one generation of workgroups at d_ff = 8192)
 constexpr int kSmallWaves = 8;   // two groups of 4 waves
 constexpr int kSmallAhead = 4;   // K slices in flight in registers (d / 64 is a multiple of 8)
 
@@ -572,10 +574,12 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
   __shared__ uint32_t ovf_s, nnz_s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 31;
+  constexpr int kNB = XR > 16 ? XR / 32 : 1;  // 32-token blocks (32x32x16 MFMAs)
   const int ng = wave & 3, kg = wave >> 2;  // neuron group (32 neurons), k-step group
   const int b = blockIdx.x;                 // TwELL tile
   const int n_t = p.F / 128;
-  const int T = static_cast<int>(p.T);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * XR;                  // first token of the block
+  const int T = static_cast<int>(min(static_cast<int64_t>(XR), p.T - t0));  // tokens in the block
   if (threadIdx.x == 0) {
     ovf_s = 0;
     nnz_s = 0;
@@ -587,7 +591,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
     const int r = min(8 * (kSmallWaves * q + wave) + (lane >> 3), 127 + XR);
     const char* base = r < 128 ? static_cast<const char*>(p.w_gate_t) +
                                      (static_cast<int64_t>(b) * 128 + r) * p.d * 2
-                               : static_cast<const char*>(p.x) + static_cast<int64_t>(min(r - 128, T - 1)) * p.d * 2;
+                               : static_cast<const char*>(p.x) + (t0 + min(r - 128, T - 1)) * p.d * 2;
     src[q] = base + ((lane & 7) ^ lds_swz(r)) * 16;  // chunk c of the row lands in swizzled place
     dst[q] = r * 128 + (lane & 7) * 16;
   }
@@ -598,11 +602,13 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
   for (int j = 0; j < kSmallAhead; ++j)
 #pragma unroll
     for (int q = 0; q < kRounds; ++q) rg[j][q] = *reinterpret_cast<const u32x4_t*>(src[q] + j * 128);
-  const bool two = XR > 32 && T > 32;
-  f32x16_t acc0, acc1;  // 32x32x16: this wave's 32 neurons x 32 tokens (acc1: tokens 32..63)
-  f32x4_t a16[2];       // 16x16x32: neurons 32 ng + 16 h .. + 15 x 16 tokens
+  const int nb_live = (T + 31) / 32;  // token blocks holding tokens of the batch
+  f32x16_t acc[kNB];  // 32x32x16: this wave's 32 neurons x tokens 32 tb .. 32 tb + 31
+  f32x4_t a16[2];     // 16x16x32: neurons 32 ng + 16 h .. + 15 x 16 tokens
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.f;
+  for (int tb = 0; tb < kNB; ++tb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[tb][r] = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) a16[0][i] = a16[1][i] = 0.f;
   auto slice = [&](int kt, u32x4_t(&v)[kRounds], bool more) {
@@ -632,18 +638,19 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
     } else {
       // k16 steps kg and kg + 2 of the slice; tokens past XR (past T) read the
       // last loaded token row, their outputs are discarded
-      Frag<EBf16> fa[2], fb0[2], fb1[2];
+      Frag<EBf16> fa[2], fb[2][kNB];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         read_frag256(fa[j], st, 32 * ng + li, kg + 2 * j, lane);
-        read_frag256(fb0[j], st, 128 + min(li, XR - 1), kg + 2 * j, lane);
-        if constexpr (XR > 32) read_frag256(fb1[j], st, 160 + li, kg + 2 * j, lane);
+#pragma unroll
+        for (int tb = 0; tb < kNB; ++tb)
+          if (tb < nb_live) read_frag256(fb[j][tb], st, 128 + min(32 * tb + li, XR - 1), kg + 2 * j, lane);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        mfma_k16(acc0, fa[j], fb0[j]);
-        if (two) mfma_k16(acc1, fa[j], fb1[j]);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int tb = 0; tb < kNB; ++tb)
+          if (tb < nb_live) mfma_k16(acc[tb], fa[j], fb[j][tb]);
     }
   };
   // the last kSmallAhead slices issue no loads (peeled, so the loop's loads are unconditional)
@@ -654,10 +661,10 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
 #pragma unroll
   for (int j = 0; j < kSmallAhead; ++j) slice(nk - kSmallAhead + j, rg[j], false);
   __syncthreads();  // every wave past its last ring reads: reuse the LDS
-  // group 1's partials at [wave ng][register][lane] (16 KB per token block),
-  // then the staged rows [64][128] bf16 at 32 KB
+  // group 1's partials at [token block][wave ng][register][lane] (16 KB per
+  // token block), then the staged rows [XR][128] bf16
   float* red = reinterpret_cast<float*>(lds);
-  uint16_t(*gl)[128] = reinterpret_cast<uint16_t(*)[128]>(lds + 32 * 1024);
+  uint16_t(*gl)[128] = reinterpret_cast<uint16_t(*)[128]>(lds + kNB * 16 * 1024);
   if (kg == 1) {
     float* o = red + ng * 1024 + lane;
     if constexpr (kM16) {
@@ -667,10 +674,11 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
         for (int i = 0; i < 4; ++i) o[(4 * h + i) * 64] = a16[h][i];
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o[r * 64] = acc0[r];
-        if (two) o[4096 + r * 64] = acc1[r];
-      }
+      for (int tb = 0; tb < kNB; ++tb)
+        if (tb < nb_live) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[tb * 4096 + r * 64] = acc[tb][r];
+        }
     }
   }
   __syncthreads();
@@ -689,17 +697,18 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
                 static_cast<uint16_t>(round_store<EBf16>(g > 0.f ? g : 0.f).bits);
         }
     } else {
-      // acc register r of lane l: neuron 32 ng + acc_row(r, l), token (block) l % 32
+      // acc register r of lane l: neuron 32 ng + acc_row(r, l), token 32 tb + l % 32
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int col = 32 * ng + acc_row(r, lane);
-        const float g0 = acc0[r] + o[r * 64];
-        if (li < T) gl[li][col] = static_cast<uint16_t>(round_store<EBf16>(g0 > 0.f ? g0 : 0.f).bits);
-        if (two) {
-          const float g1 = acc1[r] + o[4096 + r * 64];
-          if (32 + li < T) gl[32 + li][col] = static_cast<uint16_t>(round_store<EBf16>(g1 > 0.f ? g1 : 0.f).bits);
+      for (int tb = 0; tb < kNB; ++tb)
+        if (tb < nb_live) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float g = acc[tb][r] + o[tb * 4096 + r * 64];
+            if (32 * tb + li < T)
+              gl[32 * tb + li][32 * ng + acc_row(r, lane)] =
+                  static_cast<uint16_t>(round_store<EBf16>(g > 0.f ? g : 0.f).bits);
+          }
         }
-      }
     }
   }
   __syncthreads();
@@ -709,7 +718,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
   for (int t = wave; t < T; t += kSmallWaves) {
     const uint32_t v0 = gl[t][2 * lane], v1 = gl[t][2 * lane + 1];
     if (p.gate_dbg) {
-      uint16_t* gd = static_cast<uint16_t*>(p.gate_dbg) + static_cast<int64_t>(t) * p.F + b * 128 + 2 * lane;
+      uint16_t* gd = static_cast<uint16_t*>(p.gate_dbg) + (t0 + t) * p.F + b * 128 + 2 * lane;
       gd[0] = static_cast<uint16_t>(v0);
       gd[1] = static_cast<uint16_t>(v1);
     }
@@ -721,7 +730,7 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
                      static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m2 >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m2), 0u)));
     const int count = static_cast<int>(__popcll(m1) + __popcll(m2));
-    const int64_t unit = static_cast<int64_t>(t) * n_t + b;
+    const int64_t unit = (t0 + t) * n_t + b;
     const int64_t rec = unit * C;
     if (lane == 0) p.count[unit] = count;
     if (nz0 && excl < C) {
@@ -756,26 +765,29 @@ __global__ __launch_bounds__(kSmallWaves * 64, 1) void gate_pack_small_kernel(Pa
 template <int XR>
 static hipError_t launch_pack_small_t(const PackArgs& a, hipStream_t s) {
   constexpr int kRing = 2 * (128 + XR) * 128;
-  constexpr int kEpilogue = 32 * 1024 + 64 * 128 * 2;  // partial sums, then staged rows
+  constexpr int kNB = XR > 16 ? XR / 32 : 1;
+  constexpr int kEpilogue = kNB * 16 * 1024 + (XR < 64 ? 64 : XR) * 128 * 2;  // partial sums, then staged rows
   constexpr int lds = kRing > kEpilogue ? kRing : kEpilogue;
   static_assert(lds + 64 <= 160 * 1024, "LDS of one workgroup");
   static_assert(kSmallWaves == 8 && 8 % kSmallAhead == 0, "two wave groups; slices a multiple of the prefetch");
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_pack_small_kernel<XR>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gate_pack_small_kernel<XR>), dim3(a.F / 128), dim3(kSmallWaves * 64), lds, s, a);
+  const unsigned blocks = static_cast<unsigned>((a.T + XR - 1) / XR);
+  hipLaunchKernelGGL((gate_pack_small_kernel<XR>), dim3(a.F / 128, blocks), dim3(kSmallWaves * 64), lds, s, a);
   return hipGetLastError();
 }
 
 static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
   if (a.T <= 16) return launch_pack_small_t<16>(a, s);
   if (a.T <= 32) return launch_pack_small_t<32>(a, s);
-  return launch_pack_small_t<64>(a, s);
+  if (a.T <= kSmallT) return launch_pack_small_t<64>(a, s);
+  return launch_pack_small_t<128>(a, s);
 }
 
 template <class E>
 static hipError_t launch_pack_e(const PackArgs& a, hipStream_t s) {
-  if (E::kBytes == 2 && a.tile_n == 128 && a.T <= kSmallT) return launch_pack_small(a, s);
+  if (E::kBytes == 2 && a.tile_n == 128 && a.T <= kMidT) return launch_pack_small(a, s);
   const bool dbg = a.gate_dbg != nullptr;
   if (a.tile_n == 128) return dbg ? launch_pack256_t<E, true>(a, s) : launch_pack256_t<E, false>(a, s);
   return dbg ? launch_pack64_t<E, true>(a, s) : launch_pack64_t<E, false>(a, s);

@@ -1,9 +1,14 @@
 """GPU parity of the classic ELL baseline (twell_pack_classic: dense gate GEMM
 writing ReLU(g), then a conversion kernel) through the C ABI.
 
-twell_pack is pinned bit-exactly to the oracle packer elsewhere; the classic
-path must produce byte-identical TwELL planes, and its dense ReLU(g) must equal
-the pack kernel's own dense debug output (same accumulation order)."""
+twell_pack is pinned bit-exactly to the oracle packer elsewhere.  Where both
+paths run the same GEMM core (the 256-row tiles: every fp32 or T_n = 64 batch,
+and bf16 T_n = 128 batches above 512 tokens) the classic path must produce
+byte-identical TwELL planes and its dense ReLU(g) must equal the pack kernel's
+own dense debug output.  Up to 512 tokens (bf16, T_n = 128) twell_pack runs the
+small / mid-size kernel, which sums K in two groups: there each dense output
+lies within the fp32-accumulation bound of the float64 ReLU(g), and each
+path's planes are exactly the oracle packer applied to its own dense output."""
 import numpy as np
 import pytest
 import torch
@@ -44,14 +49,28 @@ def test_classic_equals_epilogue_pack(label, w):
     torch.cuda.synchronize()
     check_guards(*a1, *a2, gate, ws)
     dense = ws[: desc.T * desc.d_ff * (2 if w.dtype == "bf16" else 4)].view(desc.torch_dtype).view(desc.T, desc.d_ff)
-    assert torch.equal(dense.view(torch.int16 if w.dtype == "bf16" else torch.int32),
-                       gate.view(torch.int16 if w.dtype == "bf16" else torch.int32))
-    for p1, p2, name in zip(a1, a2, ("count", "idx", "val")):
-        b1 = p1.view(torch.uint8) if p1.dtype != torch.uint8 else p1
-        b2 = p2.view(torch.uint8) if p2.dtype != torch.uint8 else p2
-        assert torch.equal(b1, b2), name
-    if desc.T <= 1000:  # and against the oracle packer on the dense output
-        cnt, idx, val = O.twell_pack(host64(gate), desc.tile_n, desc.slots)
+    same_core = not (w.dtype == "bf16" and desc.tile_n == 128 and desc.T <= 512)
+    if same_core:
+        assert torch.equal(dense.view(torch.int16 if w.dtype == "bf16" else torch.int32),
+                           gate.view(torch.int16 if w.dtype == "bf16" else torch.int32))
+        for p1, p2, name in zip(a1, a2, ("count", "idx", "val")):
+            b1 = p1.view(torch.uint8) if p1.dtype != torch.uint8 else p1
+            b2 = p2.view(torch.uint8) if p2.dtype != torch.uint8 else p2
+            assert torch.equal(b1, b2), name
+    else:
+        # each dense output within the fp32-accumulation bound of the float64 ReLU(g) (next to
+        # zero one path may round a sum to a tiny value the other clamps to 0, so no relative test)
+        d64, g64 = host64(dense), host64(gate)
+        a_ref = O.ffn_forward(inp["x"], inp["w_gate_t"], inp["w_up_t"], inp["w_down"])["a"]
+        bound = O.gate_error_bound(inp["x"], inp["w_gate_t"], w.dtype)
+        for name, v in (("classic", d64), ("epilogue", g64)):
+            assert np.all(np.abs(v - a_ref) <= bound), f"{name} dense ReLU(g) outside the accumulation bound"
+        cnt, idx, val = O.twell_pack(g64, desc.tile_n, desc.slots)  # the pack kernel on its own output
+        assert np.array_equal(a1.count.cpu().numpy(), cnt)
+        assert np.array_equal(a1.idx.cpu().numpy(), idx)
+        assert np.array_equal(host64(a1.val), val)
+    if desc.T <= 1000:  # the classic path against the oracle packer on its own dense output
+        cnt, idx, val = O.twell_pack(host64(dense), desc.tile_n, desc.slots)
         assert np.array_equal(a2.count.cpu().numpy(), cnt)
         assert np.array_equal(a2.idx.cpu().numpy(), idx)
         assert np.array_equal(host64(a2.val), val)

@@ -116,6 +116,9 @@ CASES = [
     ("small batch T=11", W.workload(3, T=11)),
     ("small batch T=31", W.workload(3, T=31)),
     ("small batch T=57 rho 2%", W.workload(5, T=57, rho=0.02)),
+    # up to 512 tokens the same kernel runs blocks of 128 tokens (a second grid dimension)
+    ("mid batch T=129", W.workload(3, T=129)),
+    ("mid batch T=512 rho 2%", W.workload(5, T=512, rho=0.02)),
     ("c4 lognormal tail", W.workload(4, T=520)),
     ("c3 8-way neuron shard F=1024", W.workload(3, T=600, d_ff=1024)),
     ("wide d_ff=16384", W.workload(4, T=300, d_model=512, d_ff=16384)),
