@@ -535,7 +535,7 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Small and mid-size batches (T <= kMidT, bf16, T_n = 128): the work is
+// Small and mid-size batches (bf16, T_n = 128; see use_small): the work is
 // mostly reading W_gate, so the tiling is turned around.  One workgroup per
 // TwELL tile (128 neurons) and block of up to 128 tokens (one block up to 64
 // tokens); the neurons are the MFMA's M side and the tokens its N side.  With only F/128
@@ -556,7 +556,19 @@ static hipError_t launch_pack64_t(const PackArgs& a, hipStream_t s) {
 // 2l + 1, and ballots give the slots in ascending column order.  Same stored
 // values and format as the large-batch kernels.
 constexpr int kSmallT = 64;   // one token block up to here
-constexpr int kMidT = 512;    // blocks of 128 tokens up to here (one generation of workgroups at d_ff = 8192)
+constexpr int kMidT = 2048;   // blocks of 128 tokens at most up to here
+
+// Blocks of 128 tokens while all workgroups run in one generation (d_ff/128
+// tiles x token blocks <= CUs: up to 512 tokens at d_ff = 8192, 1024 at
+// 4096, 256 at 11008 on 256 CUs); a second generation made them slower than
+// the 256-row tiles (1024 tokens at d_ff = 8192).
+static bool use_small(const PackArgs& a) {
+  if (a.T <= kSmallT) return true;
+  if (a.T > kMidT) return false;
+  int cus = lockstep_resident();
+  if (cus <= 0) cus = 256;
+  return static_cast<int64_t>(a.F / 128) * ((a.T + 127) / 128) <= cus;
+}
 constexpr int kSmallWaves = 8;   // two groups of 4 waves
 constexpr int kSmallAhead = 4;   // K slices in flight in registers (d / 64 is a multiple of 8)
 
@@ -787,7 +799,7 @@ static hipError_t launch_pack_small(const PackArgs& a, hipStream_t s) {
 
 template <class E>
 static hipError_t launch_pack_e(const PackArgs& a, hipStream_t s) {
-  if (E::kBytes == 2 && a.tile_n == 128 && a.T <= kMidT) return launch_pack_small(a, s);
+  if (E::kBytes == 2 && a.tile_n == 128 && use_small(a)) return launch_pack_small(a, s);
   const bool dbg = a.gate_dbg != nullptr;
   if (a.tile_n == 128) return dbg ? launch_pack256_t<E, true>(a, s) : launch_pack256_t<E, false>(a, s);
   return dbg ? launch_pack64_t<E, true>(a, s) : launch_pack64_t<E, false>(a, s);
