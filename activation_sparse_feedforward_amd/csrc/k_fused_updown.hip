@@ -470,8 +470,14 @@ constexpr size_t token_lds_bytes() {
          static_cast<size_t>(NV) * kWave * 16;
 }
 
+// waves per SIMD the registers must allow: 4 for the 8-wave variant of rows
+// up to 4 vectors per lane (two workgroups, two tokens, share a CU), else no
+// more than one workgroup needs
 template <class E, int NV, int kW>
-__global__ __launch_bounds__(kW * kWave) void fused_updown_token_kernel(FusedArgs p) {
+constexpr int token_waves_per_simd() { return kW < kTokWaves && NV * Vec<E>::N <= 32 ? 4 : 1; }
+
+template <class E, int NV, int kW>
+__global__ __launch_bounds__(kW * kWave, (token_waves_per_simd<E, NV, kW>())) void fused_updown_token_kernel(FusedArgs p) {
   constexpr int kN = Vec<E>::N;
   constexpr int kU = NV <= 2 ? 4 : (NV <= 4 ? 2 : 1);
   constexpr int kRow = NV * kWave * kN;  // d_model
@@ -591,9 +597,8 @@ __global__ __launch_bounds__(kW * kWave) void fused_updown_token_kernel(FusedArg
   }
 }
 
-template <class E, int NV>
-static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
-  constexpr int kW = NV * Vec<E>::N <= 32 ? kTokWaves : kTokWavesWide;
+template <class E, int NV, int kW>
+static hipError_t launch_token_w(const FusedArgs& a, hipStream_t s) {
   constexpr size_t lds = token_lds_bytes<NV, E::kBytes, kW>();
   static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   static const hipError_t attr = hipFuncSetAttribute(
@@ -603,6 +608,19 @@ static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((fused_updown_token_kernel<E, NV, kW>), dim3(static_cast<unsigned>(a.T)), dim3(kW * kWave), lds, s,
                      a);
   return hipGetLastError();
+}
+
+// 16 waves per token while the batch leaves CUs idle; from kTokPairT tokens
+// on 8 waves, so that two tokens' workgroups share a CU (16 waves of 128 VGPRs
+// fit one workgroup per CU); bf16 rows wider than 2048 always 8 waves.
+constexpr int64_t kTokPairT = 512;
+
+template <class E, int NV>
+static hipError_t launch_token_t(const FusedArgs& a, hipStream_t s) {
+  if constexpr (NV * Vec<E>::N <= 32) {
+    if (a.T < kTokPairT) return launch_token_w<E, NV, kTokWaves>(a, s);
+  }
+  return launch_token_w<E, NV, kTokWavesWide>(a, s);
 }
 
 template <int NV, int TPW, int kW>
