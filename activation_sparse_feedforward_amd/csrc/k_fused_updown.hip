@@ -311,6 +311,14 @@ __global__ __launch_bounds__(kW * kWave) void fused_updown_sync_kernel(FusedArgs
   // their sweep at a different chunk (and wrap around), so the XCDs do not all
   // request the same weight rows from the MALL at the same time.
   const int n_chunks = (n_t + chunk_tiles - 1) / chunk_tiles;
+  // The barrier at each chunk keeps the workgroup's waves on the chunk's rows
+  // while those rows fill an XCD's L2.  When they take half of it or less
+  // (rows of 2 KB and narrower, e.g. bf16 d_model = 1024), the waves run free
+  // after the first chunk: the rows of the chunks the waves drift over still
+  // fit, and the waits at the barriers cost more than they save.  The first
+  // barrier stays: it orders the ranking's scratch before the first lists.
+  // The summation order does not depend on it.
+  const bool chunk_sync = int64_t(chunk_tiles) * tile_n * 2 * d * E::kBytes * 2 > kSyncChunkBytes;
   // a later generation starts one chunk earlier than the one before it, on the
   // chunk its XCD's previous generation swept last (still in L2)
   const int gen_r = p.resident > 0 ? static_cast<int>(blk / p.resident) : 0;
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(kW * kWave) void fused_updown_sync_kernel(FusedArgs
   if constexpr (kC == 16) prefetch(0);
   for (int c = 0; c < n_chunks; ++c) {
     const int b0 = ((c + rot) % n_chunks) * chunk_tiles;
-    __syncthreads();
+    if (c == 0 || chunk_sync) __syncthreads();
     const int b = b0 + lane / TPW;
     int total;
     if constexpr (kC == 16) {
