@@ -233,7 +233,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave, 2) void fused_updown_kernel
 
 // Lockstep variant (d_model up to 2048 in bf16): a workgroup of 16 waves, each
 // owning TPW tokens, walks the TwELL tiles in chunks with a workgroup barrier
-// between chunks.  Every resident workgroup therefore sweeps the neuron tiles
+// between chunks (while a chunk's rows fill an XCD's L2; narrower rows run
+// free, see chunk_sync).  Every resident workgroup therefore sweeps the neuron tiles
 // in roughly the same order at the same time, so the weight rows of the
 // current tiles (~1 MB per tile at the 2B shape) are shared through each
 // XCD's L2 instead of each wave fetching random rows from the MALL; more
